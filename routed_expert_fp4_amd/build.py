@@ -1,0 +1,35 @@
+"""Build step for libroutedfp4.so (hipcc, gfx950).
+
+Packed-fp32 instructions are disabled (``-packed-fp32-ops``); the float code is
+ordinary scalar fp32.  The library is built in-tree next to this file.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+SRC = os.path.join(HERE, "csrc", "routed_fp4.hip")
+OUT = os.path.join(HERE, "libroutedfp4.so")
+INCLUDE = os.path.join(ROOT, "include")
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-shared", f"--offload-arch={ARCH}",
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+
+
+def hipcc(src: str, out: str, extra=()) -> str:
+    tmp = out + ".tmp"
+    cmd = [HIPCC, *HIP_FLAGS, f"-I{INCLUDE}", *extra, src, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
+    os.replace(tmp, out)
+    return out
+
+
+def build_library() -> str:
+    """Compile the HIP kernels and the C ABI into libroutedfp4.so."""
+    return hipcc(SRC, OUT)

@@ -1,0 +1,325 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+Bars: routing indices and dequantised weights bit-exact; fp32 layer outputs
+within rel-L2 <= 2e-5 and max-abs <= 1e-4 * max|ref| of the oracle's fp64
+result.  Every case prints its name before it runs.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import (assert_close, cached_bank, check_selection, make_bank, route_depth, say,
+                      to_dev)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import routed_expert_fp4_amd as rf
+    rf.lib()
+    oracle.build()
+    torch.cuda.set_device(0)
+
+
+def rf():
+    import routed_expert_fp4_amd
+    return routed_expert_fp4_amd
+
+
+# ---------------------------------------------------------------------------
+# Bank bytes and dequantisation
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("name,experts", [("tiny", [0, 7]), ("w50_k16", [0, 447]),
+                                          ("k3_stack", [5])])
+def test_device_fill_matches_host(name, experts):
+    wl = synth.WORKLOADS[name]
+    spec = wl.bank(0)
+    say(f"[fill] {name} experts {experts}")
+    bank = cached_bank(spec)
+    for e in experts:
+        for t in range(7):
+            n = spec.tensor_bytes(t)
+            if n == 0:
+                continue
+            dev = bank.tensor_view(e, t, n).cpu().numpy()
+            host = synth.expert_tensor_bytes(spec, e, t).ravel()
+            assert np.array_equal(dev, host), (name, e, t)
+
+
+def _hand_bank(fmt, H, I, gate_codes, gate_scales, g=1.0):
+    """A one-expert bank whose gate matrix is given; other tensors zero."""
+    b = rf().Bank(fmt, 1, H, I)
+    b.storage.zero_()
+    b.tensor_view(0, 0, gate_codes.size).copy_(torch.from_numpy(gate_codes.ravel()))
+    b.tensor_view(0, 3, gate_scales.size).copy_(torch.from_numpy(gate_scales.ravel()))
+    if fmt == synth.FMT_NV:
+        gl = np.array([g, 1.0, 1.0], np.float32).view(np.uint8)
+        b.tensor_view(0, 6, 12).copy_(torch.from_numpy(gl))
+    return b
+
+
+def _pack(codes):
+    return (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+
+
+def _same_bits(a, b):
+    a = np.asarray(a, np.float32)
+    b = np.asarray(b, np.float32)
+    nan = np.isnan(a) & np.isnan(b)
+    return np.all(nan | (a.view(np.uint32) == b.view(np.uint32)))
+
+
+def test_dequant_mx_exhaustive():
+    """All 16 codes x all 256 e8m0 bytes (subnormal, overflow, NaN included)."""
+    say("[dequant] mx exhaustive")
+    I, H = 256, 32
+    codes = np.tile(np.arange(16, dtype=np.uint8), (I, 2))
+    scales = np.arange(256, dtype=np.uint8).reshape(I, 1)
+    b = _hand_bank(synth.FMT_MX, H, I, _pack(codes), scales)
+    out = torch.empty((I, H), dtype=torch.float32, device="cuda")
+    rf().moe_dequant(b, 0, 0, out)
+    got = out.cpu().numpy()
+    ref = oracle.dequant(synth.FMT_MX, _pack(codes), scales)
+    assert _same_bits(got, ref)
+
+
+@pytest.mark.parametrize("g", [1.0, 1.1, 1.9999999, 0.75, 3.0e-3, 1.3370001])
+def test_dequant_nv_exhaustive(g):
+    """All 16 codes x all 256 e4m3 bytes (subnormals, NaN) x a per-tensor g."""
+    say(f"[dequant] nv exhaustive g={g}")
+    I, H = 256, 32
+    codes = np.tile(np.arange(16, dtype=np.uint8), (I, 2))
+    scales = np.repeat(np.arange(256, dtype=np.uint8)[:, None], 2, 1)
+    b = _hand_bank(synth.FMT_NV, H, I, _pack(codes), scales, g)
+    out = torch.empty((I, H), dtype=torch.float32, device="cuda")
+    rf().moe_dequant(b, 0, 0, out)
+    ref = oracle.dequant(synth.FMT_NV, _pack(codes), scales, np.float32(g))
+    assert _same_bits(out.cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("name,expert", [("tiny", 3), ("w50_k16", 200), ("k3_stack", 801)])
+def test_dequant_bank_matrices(name, expert):
+    wl = synth.WORKLOADS[name]
+    spec = wl.bank(0)
+    say(f"[dequant] {name} expert {expert}")
+    bank = cached_bank(spec)
+    ref = oracle.expert_weights(spec, expert)
+    for m in range(3):
+        N, K = ref[m].shape
+        out = torch.empty((N, K), dtype=torch.float32, device="cuda")
+        rf().moe_dequant(bank, expert, m, out)
+        assert _same_bits(out.cpu().numpy(), ref[m]), (name, expert, m)
+
+
+# ---------------------------------------------------------------------------
+# Routing
+# ---------------------------------------------------------------------------
+def _ws(E, H, I, k, C):
+    return rf().Workspace(E, H, I, k, C)
+
+
+@pytest.mark.parametrize("E,k,C,seed", [(8, 2, 4, 0), (448, 16, 1, 1), (448, 8, 7, 2),
+                                        (896, 16, 16, 3), (1024, 32, 3, 4), (5, 5, 2, 5),
+                                        (64, 1, 1, 6)])
+def test_route_logits_in_bit_exact(E, k, C, seed):
+    """Selection on identical fp32 logits: indices bit-exact with the oracle's
+    fp32 selection, including planted ties and signed zeros."""
+    say(f"[route logits-in] E={E} k={k} C={C}")
+    rng = np.random.default_rng(seed)
+    L = rng.standard_normal((C, E)).astype(np.float32)
+    L[:, rng.integers(0, E, max(1, E // 8))] = L[0, 0]        # ties
+    L[0, : min(E, 4)] = 0.0
+    if E > 4:
+        L[0, 4] = -0.0
+    logits = to_dev(L)
+    idx = torch.empty((C, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((C, k), dtype=torch.float32, device="cuda")
+    rf().moe_route(None, None, logits, C, 32, E, k, idx, w, _ws(E, 32, 32, k, C))
+    got = idx.cpu().numpy()
+    ref = oracle.topk(L, k)
+    assert np.array_equal(got, ref)
+    wr = np.stack([oracle.route_weights(L[t, ref[t]].astype(np.float64)) for t in range(C)])
+    np.testing.assert_allclose(w.cpu().numpy(), wr, rtol=2e-6, atol=1e-7)
+
+
+def test_route_logits_in_all_equal_and_nan():
+    say("[route logits-in] adversarial")
+    E, k, C = 40, 6, 3
+    L = np.zeros((C, E), np.float32)
+    L[1] = np.linspace(-1, 1, E, dtype=np.float32)
+    L[1, [3, 9]] = np.nan
+    L[2] = -np.inf
+    L[2, 7] = 0.5
+    idx = torch.empty((C, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((C, k), dtype=torch.float32, device="cuda")
+    rf().moe_route(None, None, to_dev(L), C, 32, E, k, idx, w, _ws(E, 32, 32, k, C))
+    got = idx.cpu().numpy()
+    assert got[0].tolist() == list(range(k))
+    assert np.array_equal(got, oracle.topk(L, k))
+
+
+@pytest.mark.parametrize("name,C", [("tiny", 4), ("w50_k16", 1), ("w50_k8", 1),
+                                    ("w50_c7_k16", 7), ("k3_stack", 1), ("k3_stack", 16),
+                                    ("k3_stack_zipf", 1)])
+def test_route_end_to_end(name, C):
+    wl = synth.WORKLOADS[name]
+    say(f"[route e2e] {name} C={C}")
+    Wr, x = synth.layer_inputs(wl, 0, C=C)
+    logits = torch.empty((C, wl.E), dtype=torch.float32, device="cuda")
+    idx = torch.empty((C, wl.k), dtype=torch.int32, device="cuda")
+    w = torch.empty((C, wl.k), dtype=torch.float32, device="cuda")
+    rf().moe_route(to_dev(x), to_dev(Wr), logits, C, wl.H, wl.E, wl.k, idx, w,
+                   _ws(wl.E, wl.H, 32, wl.k, C))
+    L = oracle.router_logits(x, Wr)
+    bound = oracle.logit_error_bound(x, Wr, route_depth(wl.H))
+    Lg = logits.cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(Lg - L) <= bound), "fp32 logits outside the certified bound"
+    near = check_selection(L, idx.cpu().numpy(), bound, wl.k)
+    say(f"  near-tie tokens: {near} of {C}")
+    g = idx.cpu().numpy()
+    wref = np.stack([oracle.route_weights(L[t, g[t]]) for t in range(C)])
+    np.testing.assert_allclose(w.cpu().numpy(), wref, rtol=1e-3)
+
+
+# ---------------------------------------------------------------------------
+# Whole layer
+# ---------------------------------------------------------------------------
+def _layer(name, C=None, fmt=None, layer=0, pool=0):
+    wl = synth.WORKLOADS[name]
+    if fmt is not None:
+        wl = wl.with_(fmt=fmt)
+    C = wl.C if C is None else C
+    spec = wl.bank(layer)
+    bank = cached_bank(spec)
+    Wr, x = synth.layer_inputs(wl, layer, pool=pool, C=C)
+    out = torch.empty((C, wl.H), dtype=torch.float32, device="cuda")
+    idx = torch.empty((C, wl.k), dtype=torch.int32, device="cuda")
+    w = torch.empty((C, wl.k), dtype=torch.float32, device="cuda")
+    ws = _ws(wl.E, wl.H, wl.I, wl.k, C)
+    rf().moe_layer_fwd(bank, to_dev(Wr), to_dev(x), C, wl.k, out, idx, w, ws)
+    torch.cuda.synchronize()
+    return wl, spec, bank, Wr, x, out.cpu().numpy(), idx.cpu().numpy(), w.cpu().numpy(), ws
+
+
+@pytest.mark.parametrize("name,C,fmt", [
+    ("tiny", 4, None), ("tiny", 4, synth.FMT_NV), ("tiny", 1, None), ("tiny", 16, None),
+    ("w50_k16", 1, None), ("w50_k8", 1, None), ("w50_c7_k8", 7, None), ("w50_c7_k16", 7, None),
+    ("k3_stack", 1, None), ("k3_stack_zipf", 1, None),
+])
+def test_layer_parity(name, C, fmt):
+    say(f"[layer] {name} C={C} fmt={fmt}")
+    wl, spec, bank, Wr, x, out, idx, w, _ = _layer(name, C, fmt)
+    L = oracle.router_logits(x, Wr)
+    bound = oracle.logit_error_bound(x, Wr, route_depth(wl.H))
+    near = check_selection(L, idx, bound, wl.k)
+    say(f"  near-tie tokens: {near}; distinct experts: {len(np.unique(idx))}")
+    ref = oracle.layer(spec, Wr, x, wl.k, idx=idx)
+    assert_close(out, ref["out"], f"{name} C={C}")
+
+
+def test_layer_k_equals_E_and_k1():
+    say("[layer] tiny k=E and k=1")
+    for k in (8, 1):
+        wl = synth.WORKLOADS["tiny"].with_(k=k)
+        spec = wl.bank(0)
+        bank = cached_bank(spec)
+        Wr, x = synth.layer_inputs(wl, 0)
+        out = torch.empty((wl.C, wl.H), dtype=torch.float32, device="cuda")
+        idx = torch.empty((wl.C, k), dtype=torch.int32, device="cuda")
+        w = torch.empty((wl.C, k), dtype=torch.float32, device="cuda")
+        rf().moe_layer_fwd(bank, to_dev(Wr), to_dev(x), wl.C, k, out, idx, w,
+                           _ws(wl.E, wl.H, wl.I, k, wl.C))
+        ref = oracle.layer(spec, Wr, x, k)
+        assert np.array_equal(idx.cpu().numpy(), ref["idx"])
+        if k == 1:
+            assert np.all(w.cpu().numpy() == 1.0)
+        assert_close(out.cpu().numpy(), ref["out"], f"tiny k={k}")
+
+
+def test_expert_fwd_given_selection_and_invalid_slots():
+    """moe_expert_fwd with caller weights; slots naming experts outside [0, E)
+    contribute nothing."""
+    say("[expert_fwd] caller selection with invalid slots")
+    wl = synth.WORKLOADS["tiny"]
+    spec = wl.bank(0)
+    bank = cached_bank(spec)
+    _, x = synth.layer_inputs(wl, 0)
+    idx = np.array([[1, 5], [5, -1], [8, 2], [-3, 100]], np.int32)
+    w = np.array([[0.25, 0.75], [1.0, 0.5], [0.5, 0.5], [1.0, 1.0]], np.float32)
+    out = torch.empty((wl.C, wl.H), dtype=torch.float32, device="cuda")
+    rf().moe_expert_fwd(bank, to_dev(x), wl.C, wl.k, to_dev(idx), to_dev(w), out,
+                        _ws(wl.E, wl.H, wl.I, wl.k, wl.C))
+    valid = (idx >= 0) & (idx < wl.E)
+    ref = oracle.experts_forward(spec, x, np.where(valid, idx, 0), np.where(valid, w, 0.0))
+    got = out.cpu().numpy()
+    assert np.all(got[3] == 0.0)
+    assert_close(got[:3], ref[:3], "expert_fwd")
+
+
+def test_layer_deterministic_and_down_scale_doubling():
+    """Two runs are bit-identical; doubling every down-matrix e8m0 scale doubles
+    the output bit-exactly (a power-of-two scaling commutes with rounding)."""
+    say("[layer] determinism + down-scale doubling")
+    wl = synth.WORKLOADS["tiny"]
+    spec = wl.bank(0)
+    bank = make_bank(spec)
+    Wr, x = synth.layer_inputs(wl, 0)
+    ws = _ws(wl.E, wl.H, wl.I, wl.k, wl.C)
+    outs = []
+    for _ in range(2):
+        out = torch.empty((wl.C, wl.H), dtype=torch.float32, device="cuda")
+        rf().moe_layer_fwd(bank, to_dev(Wr), to_dev(x), wl.C, wl.k, out, ws=ws)
+        outs.append(out.cpu().numpy())
+    assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
+    n = spec.tensor_bytes(5)
+    for e in range(wl.E):
+        v = bank.tensor_view(e, 5, n)
+        v.add_(1)
+    out = torch.empty((wl.C, wl.H), dtype=torch.float32, device="cuda")
+    rf().moe_layer_fwd(bank, to_dev(Wr), to_dev(x), wl.C, wl.k, out, ws=ws)
+    assert np.array_equal(out.cpu().numpy(), 2 * outs[0])
+
+
+def test_layer_identical_experts():
+    """All experts share expert 3's bytes: the output no longer depends on the
+    routing (the weights sum to one)."""
+    say("[layer] identical experts")
+    wl = synth.WORKLOADS["tiny"]
+    spec = wl.bank(0)
+    bank = make_bank(spec)
+    rec = bank.storage[3 * bank.stride:(4) * bank.stride].clone()
+    for e in range(wl.E):
+        bank.storage[e * bank.stride:(e + 1) * bank.stride].copy_(rec)
+    Wr, x = synth.layer_inputs(wl, 0)
+    out = torch.empty((wl.C, wl.H), dtype=torch.float32, device="cuda")
+    rf().moe_layer_fwd(bank, to_dev(Wr), to_dev(x), wl.C, wl.k, out,
+                       ws=_ws(wl.E, wl.H, wl.I, wl.k, wl.C))
+    W = oracle.expert_weights(spec, 3)
+    ref = np.stack([oracle.expert_ffn(*W, x[t]) for t in range(wl.C)])
+    assert_close(out.cpu().numpy(), ref, "identical experts")
+
+
+def test_workspace_reuse_across_shapes():
+    """One workspace sized for the larger call serves a smaller one afterwards;
+    the counters left behind by the first call are zero again."""
+    say("[layer] workspace reuse")
+    wl = synth.WORKLOADS["tiny"]
+    spec = wl.bank(0)
+    bank = cached_bank(spec)
+    ws = _ws(wl.E, wl.H, wl.I, wl.k, 16)
+    for C in (16, 3, 1):
+        Wr, x = synth.layer_inputs(wl, 0, C=C, pool=C)
+        out = torch.empty((C, wl.H), dtype=torch.float32, device="cuda")
+        idx = torch.empty((C, wl.k), dtype=torch.int32, device="cuda")
+        rf().moe_layer_fwd(bank, to_dev(Wr), to_dev(x), C, wl.k, out, idx, None, ws)
+        ref = oracle.layer(spec, Wr, x, wl.k)
+        assert np.array_equal(idx.cpu().numpy(), ref["idx"])
+        assert_close(out.cpu().numpy(), ref["out"], f"reuse C={C}")
