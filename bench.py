@@ -1,0 +1,256 @@
+"""Decode benchmark of the routed-expert FFN on one MI355X.
+
+Workload (default): a stack of 12 MoE layers, each 896 experts, top-16,
+hidden 7168, intermediate 1536, NVFP4-style weights (~18.58 MB per expert, the
+whole 199.8 GB bank resident in HBM), batch 1 token, router logits from the
+natural router (uniform routing).  One step = one token through the 12 layers,
+12 dependent moe_layer_fwd calls on one stream.  Each step takes the next of
+16 pre-drawn tokens per layer, so consecutive steps select different experts.
+
+Prints one JSON line: the metric (MoE-layer decode us/token, with achieved HBM
+GB/s on selected-expert bytes), a roofline object for the dominant kernel work
+(the expert weight stream, timed with HIP events around moe_expert_fwd on the
+stream it runs on) and the CPU oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE layer decode µs/token + achieved HBM GB/s (% of peak), 896 experts top-16"
+HBM_PEAK_GBPS = 8000.0
+POOL = 16
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="k3_stack",
+                   help="k3_stack (uniform routing) or k3_stack_zipf (Zipf s=1.2)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-layers", type=int, default=1,
+                   help="layer-tokens of the workload the CPU oracle is timed on")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="only run a plain 2 GiB device copy (HBM counter calibration)")
+    return p.parse_args()
+
+
+def calibrate_copy():
+    import torch
+    n = 2 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"copied {n} bytes x 3")
+
+
+def expert_bytes(spec) -> int:
+    return spec.expert_bytes()
+
+
+def cpu_baseline(wl, layers: int):
+    """The oracle as it is, on `layers` layer-tokens of the workload; input
+    regeneration (the synthetic bank bytes) is excluded from the timing."""
+    import numpy as np
+    import oracle
+    import synth
+    oracle.build()
+    total = 0.0
+    for l in range(layers):
+        spec = wl.bank(l)
+        Wr, x = synth.layer_inputs(wl, l, pool=0, C=1)
+        L = oracle.router_logits(x, Wr)
+        idx = oracle.topk(L, wl.k)
+        tensors = {int(e): synth.expert_tensors(spec, int(e)) for e in idx[0]}
+        t0 = time.perf_counter()
+        L = oracle.router_logits(x, Wr)
+        idx = oracle.topk(L, wl.k)
+        w = oracle.route_weights(L[0, idx[0]])
+        ys = np.empty((wl.k, wl.H))
+        for s, e in enumerate(idx[0]):
+            t = tensors[int(e)]
+            g = t["globals"]
+            Wg = oracle.dequant(spec.fmt, t["gate_codes"], t["gate_scales"], g[0])
+            Wu = oracle.dequant(spec.fmt, t["up_codes"], t["up_scales"], g[1])
+            Wd = oracle.dequant(spec.fmt, t["down_codes"], t["down_scales"], g[2])
+            ys[s] = oracle.expert_ffn(Wg, Wu, Wd, x[0])
+        oracle.combine(w, ys)
+        total += time.perf_counter() - t0
+    us = total / layers * 1e6
+    return {"value": us, "unit": "us/token per MoE layer", "cores": int(oracle.lib().orc_threads()),
+            "kind": "oracle",
+            "sample": f"{layers} layer-token(s) of the same workload (layer 0.., pool token 0): "
+                      "router, top-k, weights, dequantisation of the 16 selected experts, their "
+                      "FFNs and the combine; bank byte regeneration not timed"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
+
+    import routed_expert_fp4_amd as rf
+    if not os.path.exists(rf.LIB_PATH):
+        from routed_expert_fp4_amd import build
+        build.build_library()
+    import synth
+    import synth.device as sd
+    if not os.path.exists(sd.LIB):
+        sd.build()
+
+    wl = synth.WORKLOADS[args.workload]
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    t_setup = time.perf_counter()
+
+    # ---- resident bank: every layer's experts in HBM ----
+    banks, wrs, xs = [], [], []
+    for l in range(wl.layers):
+        spec = wl.bank(l)
+        b = rf.Bank(wl.fmt, wl.E, wl.H, wl.I, device=dev)
+        sd.fill_bank(b.storage.data_ptr(), b.offsets, b.stride, spec, stream.cuda_stream)
+        banks.append(b)
+        Wr, x = synth.layer_inputs(wl, l, pool=0, C=POOL)
+        wrs.append(torch.from_numpy(Wr).to(dev))
+        xs.append(torch.from_numpy(x).to(dev))
+    torch.cuda.synchronize()
+    resident = sum(b.storage.numel() for b in banks)
+    need = wl.layers * wl.E * banks[0].stride
+    if resident < need:
+        raise SystemExit("bank not fully resident")
+    log(f"setup {time.perf_counter() - t_setup:.1f}s: {wl.layers} layers, "
+        f"{resident / 1e9:.1f} GB resident bank")
+
+    ws = rf.Workspace(wl.E, wl.H, wl.I, wl.k, 1, device=dev)
+    outs = [torch.empty((1, wl.H), dtype=torch.float32, device=dev) for _ in range(wl.layers)]
+
+    def step(i):
+        j = i % POOL
+        for l in range(wl.layers):
+            rf.moe_layer_fwd(banks[l], wrs[l], xs[l][j:j + 1], 1, wl.k, outs[l], ws=ws)
+
+    # ---- whole path ----
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = e0.elapsed_time(e1) / args.steps
+    us_layer = ms_step * 1000.0 / wl.layers
+
+    # ---- the expert weight stream alone (dominant work), same stream ----
+    idx = [[torch.empty((1, wl.k), dtype=torch.int32, device=dev) for _ in range(POOL)]
+           for _ in range(wl.layers)]
+    wts = [[torch.empty((1, wl.k), dtype=torch.float32, device=dev) for _ in range(POOL)]
+           for _ in range(wl.layers)]
+    for l in range(wl.layers):
+        for j in range(POOL):
+            rf.moe_route(xs[l][j:j + 1], wrs[l], None, 1, wl.H, wl.E, wl.k, idx[l][j], wts[l][j], ws)
+    torch.cuda.synchronize()
+
+    def expert_step(i):
+        j = i % POOL
+        for l in range(wl.layers):
+            rf.moe_expert_fwd(banks[l], xs[l][j:j + 1], 1, wl.k, idx[l][j], wts[l][j], outs[l], ws)
+
+    def route_step(i):
+        j = i % POOL
+        for l in range(wl.layers):
+            rf.moe_route(xs[l][j:j + 1], wrs[l], None, 1, wl.H, wl.E, wl.k, idx[l][j], wts[l][j], ws)
+
+    def timed(fn, n):
+        for i in range(max(2, args.warmup // 2)):
+            fn(i)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(n):
+            fn(i)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / (n * wl.layers) * 1000.0     # us per layer call
+
+    us_expert = timed(expert_step, args.steps)
+    us_route = timed(route_step, args.steps)
+    # distinct experts per call (C = 1: always k)
+    uniq = np.mean([len(np.unique(idx[l][j].cpu().numpy())) for l in range(wl.layers)
+                    for j in range(POOL)])
+    spec0 = wl.bank(0)
+    sel_bytes = uniq * expert_bytes(spec0)
+    router_bytes = wl.E * wl.H * 4
+    gbps_layer = sel_bytes / (us_layer * 1e-6) / 1e9
+    gbps_expert = sel_bytes / (us_expert * 1e-6) / 1e9
+
+    result = {
+        "metric": METRIC,
+        "value": round(us_layer, 3),
+        "unit": "us/token per MoE layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded NVFP4 bank generated on device, fp32 N(0,1) tokens, N(0,0.02) router)",
+        "config": {"workload": f"{wl.name}: {wl.layers} MoE layers x {wl.E} experts, top-{wl.k}, "
+                               f"H {wl.H}, I {wl.I}, NVFP4, batch 1, "
+                               + ("uniform (natural) routing" if wl.routing == "natural"
+                                  else f"Zipf s={wl.zipf_s} routing"),
+                   "layers": wl.layers, "experts": wl.E, "top_k": wl.k, "hidden": wl.H,
+                   "inter": wl.I, "format": "nvfp4", "tokens_per_call": 1},
+        "hbm_gbps_selected_expert_bytes": round(gbps_layer, 1),
+        "hbm_frac_of_peak": round(gbps_layer / HBM_PEAK_GBPS, 4),
+        "tokens_per_s": round(1000.0 / ms_step, 2),
+        "selected_expert_bytes_per_layer": int(sel_bytes),
+        "router_bytes_per_layer": router_bytes,
+        "us_per_layer_route": round(us_route, 3),
+        "us_per_layer_experts": round(us_expert, 3),
+        "roofline": {"bound": "hbm", "achieved": round(gbps_expert, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(gbps_expert / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "expert weight stream: moe_expert_fwd per layer call "
+                               "(k_dispatch + k_gate_up + k_down + k_zero_uncovered), "
+                               "16 x 18,579,468 selected-expert bytes per launch set"},
+        "wall_s_timed": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle ...")
+        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_layers)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

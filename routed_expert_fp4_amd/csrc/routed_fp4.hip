@@ -38,12 +38,13 @@ constexpr int kDnRowsPerGroup = 4; // down: rows per 16-lane group
 constexpr int kDnRows = 16 * kDnRowsPerGroup;  // down: H rows per item
 constexpr int kXsFloats = 10240;   // LDS floats for staged activations (40 KiB)
 constexpr int kRouteXs = 8192;     // LDS floats for the router's x tile (32 KiB)
+constexpr int kLogitCopies = 16;   // batch-1 kernel: replicas of the tagged logits
 
 // ---------------------------------------------------------------------------
 // Workspace layout
 // ---------------------------------------------------------------------------
 struct WsLayout {
-  size_t ctrl, dtick, lpart, logits, idx, w, disp, h, part, total;
+  size_t ctrl, dtick, lpart, logits, idx, w, disp, h, part, tlogits, th, tpart, total;
 };
 
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
@@ -61,6 +62,10 @@ WsLayout ws_layout(int E, int H, int I, int k, int C) {
   L.disp = o;   o = align256(o + (16 + 2 * CK + CK * C) * sizeof(int32_t));
   L.h = o;      o = align256(o + CK * I * sizeof(float));
   L.part = o;   o = align256(o + CK * H * sizeof(float));
+  // batch-1 kernel: (epoch, value) words
+  L.tlogits = o; o = align256(o + (size_t)kLogitCopies * E * sizeof(uint64_t));
+  L.th = o;      o = align256(o + (size_t)k * I * sizeof(uint64_t));
+  L.tpart = o;   o = align256(o + (size_t)k * H * sizeof(uint64_t));
   L.total = o;
   return L;
 }
@@ -82,14 +87,9 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t b) {
 }
 
 __device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
-  // OCP fp8 e4m3 ("FN"): bias 7, no infinities, S.1111.111 is NaN.
-  const uint32_t s = (b & 0x80u) << 24, E = (b >> 3) & 15u, m = b & 7u;
-  if (E == 15u && m == 7u) return __uint_as_float(0x7FC00000u);
-  if (E == 0u) {
-    const float v = (float)m * 0x1p-9f;          // (m/8) * 2^-6, exact
-    return __uint_as_float(__float_as_uint(v) | s);
-  }
-  return __uint_as_float(s | ((E + 120u) << 23) | (m << 20));
+  // OCP fp8 e4m3 ("FN": bias 7, no infinities, S.1111.111 is NaN), decoded by
+  // the hardware conversion of the low byte.
+  return __builtin_amdgcn_cvt_f32_fp8((int)(b & 0xFFu), 0);
 }
 
 // Two e2m1 elements of byte `sel` of `w`: element 2j (bits 3..0) in .x and
@@ -121,6 +121,49 @@ __device__ __forceinline__ uint32_t logit_key(float l) {
   uint32_t u = __float_as_uint(l);
   if ((u & 0x7FFFFFFFu) == 0u) u = 0u;
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Cross-workgroup hand-off without cache-maintenance fences.  An agent-scope
+// fence on gfx950 writes back and invalidates the XCD's L2 (about a
+// microsecond, serialised per XCD), so the kernels never use one.  Instead the
+// data one workgroup hands to another is written with agent-coherent stores
+// (sc1), each producer waits for its stores to complete before it takes a
+// ticket with a relaxed device-scope atomic, and the consumer that draws the
+// last ticket reads the data with agent-coherent loads.
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Bulk coherent reads go through buffer loads with the sc1 cache-policy bit:
+// unlike atomic loads they are not serialised one round trip at a time.
+// (Buffer resource word 3 for gfx9-family raw buffers; out-of-range offsets
+// read zero.)
+constexpr int kCachePolicySc1 = 16;
+constexpr int kCachePolicyNt = 2;   // non-temporal: weights are read once per call
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_view(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ float coherent_ld(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)byte_off, 0, kCachePolicySc1));
+}
+__device__ __forceinline__ float4 coherent_ld4(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, kCachePolicySc1);
+  return make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]),
+                     __uint_as_float(v[3]));
+}
+// All of this workgroup's stores are complete, then one ticket; returns true
+// (in every thread) for the workgroup that drew ticket n-1.
+__device__ __forceinline__ bool last_to_arrive(uint32_t* ticket, uint32_t n, int* s_flag) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0)
+    *s_flag = (__hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+               n - 1u) ? 1 : 0;
+  __syncthreads();
+  return *s_flag != 0;
+}
+__device__ __forceinline__ void reset_ticket(uint32_t* ticket) {
+  __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave (lane order).
@@ -156,38 +199,23 @@ struct TopkShared {
   int32_t sel_e[4][32];
   float sel_l[4][32];
   float sorted_l[4][32];
+  int32_t sorted_e[32];
   int32_t sidx[MOE_MAX_DECODE_TOKENS * MOE_MAX_TOPK];
   int32_t first[MOE_MAX_EXPERTS];
   int32_t uexp[MOE_MAX_DECODE_TOKENS * MOE_MAX_TOPK];
   int32_t wtot[4];
 };
 
-// Top-k of one token by one wave (all four waves call this together, with
-// `active` false for waves without a token; barriers are workgroup-wide).
-// Selection is exact on the fp32 logits: a 4-pass, 8-bit radix select finds
-// the k-th largest key; keys above it are taken, equal keys by lowest index;
-// the k winners are ranked by (key desc, index asc).
-__device__ void topk_token(const RouteArgs& a, TopkShared& S, int t, bool active) {
+// Top-k over the E values one wave holds (value e in lane e%64, slot e/64, as
+// orderable keys `key` and raw logits `lv`).  All four waves call this together,
+// with `active` false for waves that have no token; barriers are workgroup-wide.
+// Selection is exact on the fp32 logits: a 4-pass, 8-bit radix select finds the
+// k-th largest key; keys above it are taken, equal keys by lowest index; the k
+// winners are ranked by (key desc, index asc).  Output, in rank order:
+// S.sel_e[wave][0..k) and S.sorted_l[wave][0..k).
+__device__ void wave_topk(TopkShared& S, const uint32_t (&key)[16], const float (&lv)[16],
+                          int E, int k, bool active) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int E = a.E, k = a.k;
-  uint32_t key[16];
-  float lv[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int e = lane + 64 * i;
-    float l = 0.0f;
-    if (active && e < E) {
-      if (a.x) {
-        l = a.lpart[(size_t)t * E + e];
-        for (int s = 1; s < a.ksplit; ++s) l += a.lpart[((size_t)s * a.C + t) * E + e];
-        if (a.logits_out) a.logits_out[(size_t)t * E + e] = l;
-      } else {
-        l = a.logits_in[(size_t)t * E + e];
-      }
-    }
-    lv[i] = l;
-    key[i] = logit_key(l);
-  }
   uint32_t prefix = 0, pmask = 0;
   int r = k;
   for (int pass = 0; pass < 4; ++pass) {
@@ -258,24 +286,125 @@ __device__ void topk_token(const RouteArgs& a, TopkShared& S, int t, bool active
   }
   __syncthreads();
   // rank the k winners: (key desc, index asc)
+  int my_e = 0, rank = 0;
+  float my_l = 0.0f;
   if (active && lane < k) {
     const uint32_t mk = S.sel_key[wave][lane];
-    const int me = S.sel_e[wave][lane];
-    int rank = 0;
+    my_e = S.sel_e[wave][lane];
+    my_l = S.sel_l[wave][lane];
     for (int j = 0; j < k; ++j) {
       const uint32_t kj = S.sel_key[wave][j];
       const int ej = S.sel_e[wave][j];
-      rank += (kj > mk || (kj == mk && ej < me)) ? 1 : 0;
+      rank += (kj > mk || (kj == mk && ej < my_e)) ? 1 : 0;
     }
-    a.idx_out[(size_t)t * k + rank] = me;
-    S.sidx[t * k + rank] = me;
-    S.sorted_l[wave][rank] = S.sel_l[wave][lane];
   }
   __syncthreads();
+  if (active && lane < k) {
+    S.sel_e[wave][rank] = my_e;
+    S.sorted_l[wave][rank] = my_l;
+  }
+  __syncthreads();
+}
+
+// Wave-wide max / min of a 32-bit value with DPP row shifts and row
+// broadcasts (lane 63 ends with the result; every lane receives it).
+template <bool MAX>
+__device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v) {
+  const int id = MAX ? 0 : -1;   // identity for lanes without a source
+  auto op = [](uint32_t a, uint32_t b) { return MAX ? (a > b ? a : b) : (a < b ? a : b); };
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x111, 0xF, 0xF, false));  // row_shr:1
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x112, 0xF, 0xF, false));  // row_shr:2
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x114, 0xF, 0xF, false));  // row_shr:4
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x118, 0xF, 0xF, false));  // row_shr:8
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x142, 0xA, 0xF, false));  // row_bcast:15
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x143, 0xC, 0xF, false));  // row_bcast:31
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// Exact top-k of up to 64*N (key, index, logit) entries held N per lane by one
+// wave: each lane sorts its entries by (key desc, index asc), then k rounds
+// each take the best lane head (wave max of the keys; equal keys go to the
+// lowest index) and pop it.  Empty entries are (0, 0xFFFF).  Results land in
+// out_key / out_e / out_l [0, k) in rank order.
+template <int N>
+__device__ void wave_tournament(uint32_t (&key)[N], uint32_t (&ix)[N], float (&lv)[N], int k,
+                                uint32_t* out_key, int32_t* out_e, float* out_l) {
+  const int lane = threadIdx.x & 63;
+  // odd-even transposition sort of the lane's N entries (N is tiny)
+#pragma unroll
+  for (int pass = 0; pass < N; ++pass) {
+#pragma unroll
+    for (int i = pass & 1; i + 1 < N; i += 2) {
+      const bool sw = key[i] < key[i + 1] || (key[i] == key[i + 1] && ix[i] > ix[i + 1]);
+      const uint32_t k0 = sw ? key[i + 1] : key[i], k1 = sw ? key[i] : key[i + 1];
+      const uint32_t i0 = sw ? ix[i + 1] : ix[i], i1 = sw ? ix[i] : ix[i + 1];
+      const float l0 = sw ? lv[i + 1] : lv[i], l1 = sw ? lv[i] : lv[i + 1];
+      key[i] = k0; key[i + 1] = k1; ix[i] = i0; ix[i + 1] = i1; lv[i] = l0; lv[i + 1] = l1;
+    }
+  }
+  for (int s = 0; s < k; ++s) {
+    const uint32_t m = wave_reduce_u32<true>(key[0]);
+    const unsigned long long tied = __ballot(key[0] == m);
+    uint32_t we;
+    if (__popcll(tied) == 1) we = (uint32_t)__shfl((int)ix[0], __ffsll((long long)tied) - 1, 64);
+    else we = wave_reduce_u32<false>(key[0] == m ? ix[0] : 0xFFFFFFFFu);
+    const bool win = key[0] == m && ix[0] == we;
+    if (win) {
+      out_key[s] = m;
+      out_e[s] = (int32_t)we;
+      out_l[s] = lv[0];
+#pragma unroll
+      for (int i = 0; i + 1 < N; ++i) { key[i] = key[i + 1]; ix[i] = ix[i + 1]; lv[i] = lv[i + 1]; }
+      key[N - 1] = 0u;
+      ix[N - 1] = 0xFFFFu;
+      lv[N - 1] = 0.0f;
+    }
+  }
+  (void)lane;
+}
+
+// sigmoid(l_s) / sum over the k of sigmoid(l), for lane s < k of a wave
+// (the same value in every lane's sum: the butterfly adds pairs commutatively).
+__device__ __forceinline__ float route_weight(float l, int lane, int k) {
+  const float sg = (lane < k) ? 1.0f / (1.0f + expf(-l)) : 0.0f;
+  return sg / wave_sum(sg);
+}
+
+// Top-k of token t by one wave of the router's last workgroup.
+__device__ void topk_token(const RouteArgs& a, TopkShared& S, int t, bool active) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int E = a.E, k = a.k;
+  uint32_t key[16];
+  float lv[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int e = lane + 64 * i;
+    float l = 0.0f;
+    if (active && e < E) {
+      if (a.x) {
+        const __amdgpu_buffer_rsrc_t lp =
+            coherent_view(a.lpart, (uint32_t)((size_t)a.ksplit * a.C * E * sizeof(float)));
+        l = coherent_ld(lp, (uint32_t)(((size_t)t * E + e) * 4));
+        for (int s = 1; s < a.ksplit; ++s)
+          l += coherent_ld(lp, (uint32_t)((((size_t)s * a.C + t) * E + e) * 4));
+        if (a.logits_out) a.logits_out[(size_t)t * E + e] = l;
+      } else {
+        l = a.logits_in[(size_t)t * E + e];
+      }
+    }
+    lv[i] = l;
+    key[i] = logit_key(l);
+  }
+  wave_topk(S, key, lv, E, k, active);
   if (active) {
-    const float sg = (lane < k) ? 1.0f / (1.0f + expf(-S.sorted_l[wave][lane])) : 0.0f;
-    const float tot = wave_sum(sg);
-    if (lane < k) a.w_out[(size_t)t * k + lane] = sg / tot;
+    const float l = (lane < k) ? S.sorted_l[wave][lane] : 0.0f;
+    const float w = route_weight(l, lane, k);
+    if (lane < k) {
+      const int e = S.sel_e[wave][lane];
+      a.idx_out[(size_t)t * k + lane] = e;
+      a.w_out[(size_t)t * k + lane] = w;
+      S.sidx[t * k + lane] = e;
+    }
   }
 }
 
@@ -381,21 +510,16 @@ __global__ __launch_bounds__(kWG) void k_route(RouteArgs a) {
     for (int t = 0; t < CM; ++t) {
       if (t < a.C) {
         const float v = wave_sum(acc[t]);
-        if (lane == 0 && e < a.E) a.lpart[((size_t)ks * a.C + t) * a.E + e] = v;
+        if (lane == 0 && e < a.E) store_coherent(&a.lpart[((size_t)ks * a.C + t) * a.E + e], v);
       }
     }
     // the last workgroup to finish runs the selection
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) s_last = (atomicAdd(&a.ctrl[0], 1u) == gridDim.x - 1) ? 1 : 0;
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
+    if (!last_to_arrive(&a.ctrl[0], gridDim.x, &s_last)) return;
   }
   for (int t0 = 0; t0 < a.C; t0 += 4) topk_token(a, S, t0 + wave, t0 + wave < a.C);
   __syncthreads();
   if (a.disp) build_dispatch(S, a.disp, a.C, a.k, a.E);
-  if (a.x && tid == 0) atomicExch(&a.ctrl[0], 0u);
+  if (a.x && tid == 0) reset_ticket(&a.ctrl[0]);
 }
 
 // Dispatch table from a caller-given selection (moe_expert_fwd).
@@ -657,7 +781,7 @@ __device__ void down_item(const ExpArgs& a, float* xs, int e, int rb, const int*
       const float y = group16_sum(acc[r][i]);
       if (l16 == 0 && i < nt && jr[r] < H) {
         const int p = pairs[i];
-        a.part[(size_t)p * H + jr[r]] = a.w[p] * (gd * y);
+        store_coherent(&a.part[(size_t)p * H + jr[r]], a.w[p] * (gd * y));
       }
     }
   }
@@ -683,26 +807,24 @@ __global__ __launch_bounds__(kWG) void k_down(ExpArgs a) {
       else down_item<FMT, (NTMAX >= 4 ? 4 : 1)>(a, xs, e, rb, pairs + g0, nt);
     }
     // the last distinct expert to finish this row block sums the slots
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) s_last = (atomicAdd(&a.dtick[rb], 1u) == (uint32_t)(nu - 1)) ? 1 : 0;
-    __syncthreads();
-    if (s_last) {
-      __threadfence();
+    if (last_to_arrive(&a.dtick[rb], (uint32_t)nu, &s_last)) {
       const int j0 = rb * kDnRows;
       for (int q = threadIdx.x; q < a.C * kDnRows; q += kWG) {
         const int t = q / kDnRows, j = j0 + (q - t * kDnRows);
         if (j < a.H) {
+          const __amdgpu_buffer_rsrc_t pv =
+              coherent_view(a.part, (uint32_t)((size_t)a.C * a.k * a.H * sizeof(float)));
           float s = 0.0f;
           for (int sl = 0; sl < a.k; ++sl) {
             const int p = t * a.k + sl;
             const int ee = a.idx[p];
-            if (ee >= 0 && ee < a.E) s += a.part[(size_t)p * a.H + j];
+            const float v = coherent_ld(pv, (uint32_t)(((size_t)p * a.H + j) * 4));
+            if (ee >= 0 && ee < a.E) s += v;
           }
           a.out[(size_t)t * a.H + j] = s;
         }
       }
-      if (threadIdx.x == 0) atomicExch(&a.dtick[rb], 0u);
+      if (threadIdx.x == 0) reset_ticket(&a.dtick[rb]);
     }
   }
 }
@@ -718,6 +840,604 @@ __global__ void k_zero_uncovered(ExpArgs a) {
   }
   if (any) return;
   for (int j = threadIdx.x; j < a.H; j += blockDim.x) a.out[(size_t)t * a.H + j] = 0.0f;
+}
+
+// ---------------------------------------------------------------------------
+// Batch-1 decode: the whole layer as one cooperative kernel
+// ---------------------------------------------------------------------------
+// Hand-offs between workgroups carry the call's epoch: a producer writes
+// (epoch, value) as one 64-bit agent-coherent store and moves on; a consumer
+// polls until every value it needs carries the current epoch.  No producer
+// ever waits for its stores and no work item takes a ticket.  The last
+// workgroup to exit advances the epoch for the next call.
+enum { kCtrlRouteTicket = 0, kCtrlExit = 3, kCtrlErr = 4, kCtrlEpoch = 5 };
+constexpr int kG1 = 256;                  // workgroups of the batch-1 kernel (one per CU)
+constexpr int kWG1 = 512;                 // threads per batch-1 workgroup (8 waves)
+constexpr int kMaxH1 = 8192;              // batch-1 kernel limits
+constexpr int kMaxI1 = 4096;
+constexpr uint32_t kSpinLimit = 1u << 22; // ~seconds: a wait that never ends gives up
+
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// Weight bytes are read once per call: non-temporal loads keep them from
+// displacing the activations and hand-off data in the caches.
+__device__ __forceinline__ uint4 load_stream16(const uint8_t* p) {
+  const u32x4_t t = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(t.x, t.y, t.z, t.w);
+}
+__device__ __forceinline__ float4 load_stream16f(const float* p) {
+  const f32x4_t t = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
+  return make_float4(t.x, t.y, t.z, t.w);
+}
+template <int FMT>
+__device__ __forceinline__ uint32_t load_scales_stream(const uint8_t* srow, int c) {
+  if (FMT == MOE_FMT_MXFP4) return __builtin_nontemporal_load(srow + c);
+  return __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(srow + 2 * c));
+}
+
+// (epoch, fp32) hand-off words
+__device__ __forceinline__ void store_tagged(uint64_t* p, uint32_t epoch, float v) {
+  __hip_atomic_store(p, ((uint64_t)epoch << 32) | __float_as_uint(v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+// two tagged words with one 16-byte coherent load: {lo0, epoch0, lo1, epoch1}
+__device__ __forceinline__ uint4 coherent_ld_u4(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, kCachePolicySc1);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ uint2 coherent_ld_u2(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)byte_off, 0, kCachePolicySc1);
+  return make_uint2(v[0], v[1]);
+}
+
+struct Moe1Args {
+  const uint8_t* base;
+  int64_t stride;
+  int64_t off[MOE_NUM_TENSORS];
+  int E, H, I, k;
+  const float* x;          // [H]
+  const float* Wr;         // [E][H], or null: selection given in idx_in / w_in
+  const int32_t* idx_in;   // [k]
+  const float* w_in;       // [k]
+  int32_t* idx_out;        // [k] or null
+  float* w_out;            // [k] or null
+  uint64_t* tlogits;       // ws [E]      tagged router logits
+  uint64_t* th;            // ws [k][I]   tagged intermediate activations
+  uint64_t* tpart;         // ws [k][H]   tagged per-slot down outputs
+  float* out;              // [H]
+  uint32_t* ctrl;
+  int n_router;
+};
+
+struct Moe1Shared {
+  union {
+    float xs[kMaxH1 + kMaxH1 / 8];   // x, padded 4 floats per 32 (router, gate/up)
+    float hs[kMaxI1 + kMaxI1 / 8];   // h of the slot (down)
+  } u;
+  TopkShared topk;
+  float ys[kWG1];                  // the combining slice's own rows (R <= kWG1)
+  int32_t sidx[MOE_MAX_TOPK];
+  float sw[MOE_MAX_TOPK];
+  float red[8];
+  int flag;
+};
+
+__device__ __forceinline__ bool wg_any(bool v, int* s_flag) {
+  if (threadIdx.x == 0) *s_flag = 0;
+  __syncthreads();
+  if (v) *s_flag = 1;
+  __syncthreads();
+  return *s_flag != 0;
+}
+
+// Router rows e0, e0 + kG1, e0 + 2*kG1, e0 + 3*kG1 (those below E) at once:
+// wave w takes half (w & 1) of row w >> 1, so every weight load of the four
+// rows is in flight together; the two halves are added in a fixed order and
+// the logit is written, tagged, to every replica.
+__device__ void moe1_router_rows(const Moe1Args& a, Moe1Shared& S, int e0, uint32_t epoch) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r = wave >> 1, half = wave & 1;
+  const int e = e0 + r * kG1;
+  const int q = a.H / 2;                          // this wave's half of K
+  constexpr int RU = kMaxH1 / 2 / 4 / 64;         // float4 loads per lane (max)
+  float acc = 0.0f;
+  if (e < a.E) {
+    const __amdgpu_buffer_rsrc_t wr =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(a.Wr + (size_t)e * a.H), (short)0,
+                                          a.H * 4, 0x00020000);
+    const uint32_t woff = (uint32_t)(half * q + lane * 4) * 4;
+    float4 wv[RU];
+#pragma unroll
+    for (int u = 0; u < RU; ++u) {
+      const int c = (lane + 64 * u) * 4;
+      if (c < q) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(wr, (int)(woff + 1024 * u), 0,
+                                                             kCachePolicyNt);
+        wv[u] = make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]),
+                            __uint_as_float(v[3]));
+      } else {
+        wv[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < RU; ++u) {
+      const int c = (lane + 64 * u) * 4;
+      if (c < q) {
+        const int col = half * q + c;
+        const float4 xv = *reinterpret_cast<const float4*>(&S.u.xs[col + (col >> 5) * 4]);
+        acc += wv[u].x * xv.x + wv[u].y * xv.y + wv[u].z * xv.z + wv[u].w * xv.w;
+      }
+    }
+  }
+  acc = wave_sum(acc);
+  if (lane == 0) S.red[wave] = acc;
+  __syncthreads();
+  if (threadIdx.x < 4 * kLogitCopies) {
+    const int rr = threadIdx.x / kLogitCopies, copy = threadIdx.x % kLogitCopies;
+    const int er = e0 + rr * kG1;
+    if (er < a.E)
+      store_tagged(&a.tlogits[(size_t)copy * a.E + er], epoch, S.red[2 * rr] + S.red[2 * rr + 1]);
+  }
+  __syncthreads();
+}
+
+// The selection, computed by every workgroup for itself from the tagged
+// logits (or taken from the caller when the selection is given).
+__device__ void moe1_routing(const Moe1Args& a, Moe1Shared& S, uint32_t epoch, bool writer) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int k = a.k;
+  if (a.Wr) {
+    // wave w holds experts w*256 + lane + 64*i, i < 4
+    uint32_t key[4], ix[4];
+    float lv[4];
+    const __amdgpu_buffer_rsrc_t lr = coherent_view(
+        a.tlogits + (size_t)(blockIdx.x % kLogitCopies) * a.E, (uint32_t)a.E * 8);
+    for (uint32_t it = 0;; ++it) {
+      bool missing = false;
+      uint2 t[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) t[i] = coherent_ld_u2(lr, (uint32_t)(wave * 256 + lane + 64 * i) * 8);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = wave * 256 + lane + 64 * i;
+        if (wave < 4 && e < a.E) {
+          missing |= t[i].y != epoch;
+          lv[i] = __uint_as_float(t[i].x);
+          key[i] = logit_key(lv[i]);
+          ix[i] = (uint32_t)e;
+        } else {
+          lv[i] = 0.0f;
+          key[i] = 0u;
+          ix[i] = 0xFFFFu;
+        }
+      }
+      if (!wg_any(missing, &S.flag)) break;
+      if (it == kSpinLimit) {
+        if (threadIdx.x == 0)
+          __hip_atomic_store(&a.ctrl[kCtrlErr], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+    TopkShared& T = S.topk;
+    if (wave < 4) wave_tournament<4>(key, ix, lv, k, T.sel_key[wave], T.sel_e[wave], T.sel_l[wave]);
+    __syncthreads();
+    if (wave == 0) {
+      // merge the 4 waves' k best (4k <= 128 entries, two per lane)
+      uint32_t mk[2], mi[2];
+      float ml[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int c = lane + 64 * h;          // candidate c: wave c / k, rank c % k
+        const int w = c / k, r = c - w * k;
+        if (w < 4) {
+          mk[h] = T.sel_key[w][r]; mi[h] = (uint32_t)T.sel_e[w][r]; ml[h] = T.sel_l[w][r];
+        } else {
+          mk[h] = 0u; mi[h] = 0xFFFFu; ml[h] = 0.0f;
+        }
+      }
+      // (reading all of sel_* before the merge writes its results elsewhere)
+      wave_tournament<2>(mk, mi, ml, k, T.hist[0], T.sorted_e, T.sorted_l[0]);
+      const float l = (lane < k) ? T.sorted_l[0][lane] : 0.0f;
+      const float w = route_weight(l, lane, k);
+      if (lane < k) {
+        const int e = T.sorted_e[lane];
+        S.sidx[lane] = e;
+        S.sw[lane] = w;
+        if (writer && a.idx_out) a.idx_out[lane] = e;
+        if (writer && a.w_out) a.w_out[lane] = w;
+      }
+    }
+  } else if (threadIdx.x < k) {
+    S.sidx[threadIdx.x] = a.idx_in[threadIdx.x];
+    S.sw[threadIdx.x] = a.w_in[threadIdx.x];
+  }
+  __syncthreads();
+}
+
+// acc[r] += sum over one 32-element chunk of w_r * x for NR rows and one token,
+// one 8-element dword at a time (the barrier keeps the conversions of later
+// dwords from being hoisted, which would hold a register per value).
+template <int FMT, int NR>
+__device__ __forceinline__ void chunk_fma1(const uint4 (&q)[NR], const uint32_t (&sc)[NR],
+                                           const float* xs, int xoff, float (&acc)[NR][1]) {
+  const float4* x4 = reinterpret_cast<const float4*>(xs + xoff);
+  float blk[NR];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    if ((d & 1) == 0) {
+#pragma unroll
+      for (int r = 0; r < NR; ++r) blk[r] = 0.0f;
+    }
+    const float4 xa = x4[2 * d];
+    const float4 xb = x4[2 * d + 1];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const uint32_t wd = (d == 0) ? q[r].x : (d == 1) ? q[r].y : (d == 2) ? q[r].z : q[r].w;
+      const float2 v0 = fp4x2<0>(wd), v1 = fp4x2<1>(wd), v2 = fp4x2<2>(wd), v3 = fp4x2<3>(wd);
+      float b = blk[r];
+      b += v0.x * xa.x; b += v0.y * xa.y; b += v1.x * xa.z; b += v1.y * xa.w;
+      b += v2.x * xb.x; b += v2.y * xb.y; b += v3.x * xb.z; b += v3.y * xb.w;
+      blk[r] = b;
+    }
+    if (d & 1) {
+      // one scale per 16 elements: NV has its own byte per half, MX shares one
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        const float s = (FMT == MOE_FMT_NVFP4) ? e4m3_to_f32((sc[r] >> (8 * (d >> 1))) & 0xFFu)
+                                               : e8m0_to_f32(sc[r]);
+        acc[r][0] += s * blk[r];
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Software-pipelined weight stream: lane l16 of a 16-lane group owns chunks
+// c = l16 + 16*i (i < KCH) of each of NR rows; the chunks go in stages of PB,
+// and the loads of stage s+1 are in flight while stage s is multiplied.  KCH
+// is a compile-time constant, so the whole stream is straight-line code.
+// The loads are buffer loads: one descriptor per tensor (scalar registers),
+// one 32-bit offset per row, and the chunk stride in the instruction's
+// immediate offset, so no per-chunk 64-bit address is ever materialised.
+template <int FMT, int NR, int KCH, int PB>
+struct RowStream {
+  static constexpr int NST = (KCH + PB - 1) / PB;
+  __amdgpu_buffer_rsrc_t crs[NR];   // code tensor of row r
+  __amdgpu_buffer_rsrc_t srs[NR];   // scale tensor of row r
+  uint32_t coff[NR];                // byte offset of (row r, chunk l16) in crs[r]
+  uint32_t soff[NR];                // byte offset of its scale byte(s) in srs[r]
+  __device__ __forceinline__ void load(int st, uint4 (&q)[PB][NR], uint32_t (&sc)[PB][NR]) const {
+#pragma unroll
+    for (int b = 0; b < PB; ++b) {
+      const int i = st * PB + b;
+      if (i < KCH) {
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+          const auto v = __builtin_amdgcn_raw_buffer_load_b128(crs[r], (int)(coff[r] + 256 * i), 0,
+                                                               kCachePolicyNt);
+          q[b][r] = make_uint4(v[0], v[1], v[2], v[3]);
+          if (FMT == MOE_FMT_MXFP4)
+            sc[b][r] = __builtin_amdgcn_raw_buffer_load_b8(srs[r], (int)(soff[r] + 16 * i), 0,
+                                                          kCachePolicyNt);
+          else
+            sc[b][r] = __builtin_amdgcn_raw_buffer_load_b16(srs[r], (int)(soff[r] + 32 * i), 0,
+                                                           kCachePolicyNt);
+        }
+      }
+    }
+  }
+  __device__ __forceinline__ void fma(int st, const uint4 (&q)[PB][NR], const uint32_t (&sc)[PB][NR],
+                                      const float* xs, float (&acc)[NR][1]) const {
+    const int l16 = threadIdx.x & 15;
+#pragma unroll
+    for (int b = 0; b < PB; ++b) {
+      if (st * PB + b < KCH) {
+        const int c = l16 + 16 * (st * PB + b);
+        chunk_fma1<FMT, NR>(q[b], sc[b], xs, c * 36, acc);
+      }
+    }
+  }
+  // all stages; stage 0 may already be loaded into q0
+  __device__ __forceinline__ void run(const float* xs, float (&acc)[NR][1], uint4 (&q0)[PB][NR],
+                                      uint32_t (&s0)[PB][NR], bool stage0_loaded) const {
+    uint4 q1[PB][NR];
+    uint32_t s1[PB][NR];
+    if (!stage0_loaded) load(0, q0, s0);
+    // the barriers pin the pipeline: stage s+1's loads are issued just before
+    // stage s is multiplied, never earlier (earlier would need more registers)
+#pragma unroll
+    for (int st = 0; st < NST; ++st) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (st & 1) {
+        if (st + 1 < NST) load(st + 1, q0, s0);
+        __builtin_amdgcn_sched_barrier(0);
+        fma(st, q1, s1, xs, acc);
+      } else {
+        if (st + 1 < NST) load(st + 1, q1, s1);
+        __builtin_amdgcn_sched_barrier(0);
+        fma(st, q0, s0, xs, acc);
+      }
+    }
+  }
+};
+
+// One tensor of one expert as a buffer descriptor.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tensor_view(const uint8_t* rec, int64_t off,
+                                                              uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(rec + off), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+constexpr int kGuStage = 4;   // chunks per lane per pipeline stage (gate/up)
+constexpr int kDnStage = 8;   // (down, one row per lane group at a time)
+
+// Streamed dot products of one 16-lane group over NSEG consecutive segments
+// (segment s = NR rows, one per row stream r, at offset coff[r] + s*seg_stride);
+// lane l16 reads chunks l16 + 16*i (i < KCH) of each row.  The NSEG*KCH chunks
+// run as one pipeline in stages of PB: the loads of stage t+1 are in flight
+// while stage t is multiplied, across segment boundaries too.  After the last
+// chunk of a segment, done(s, acc) receives the lane's partial sums.
+template <int FMT, int NR, int NSEG, int KCH, int PB>
+struct SegStream {
+  static constexpr int NF = NSEG * KCH;
+  static constexpr int NST = (NF + PB - 1) / PB;
+  __amdgpu_buffer_rsrc_t crs[NR];
+  __amdgpu_buffer_rsrc_t srs[NR];
+  uint32_t coff[NR], soff[NR];       // segment 0, this lane's first chunk
+  uint32_t seg_stride, seg_sstride;  // bytes between segments (codes, scales)
+  __device__ __forceinline__ void load(int st, uint4 (&q)[PB][NR], uint32_t (&sc)[PB][NR]) const {
+#pragma unroll
+    for (int b = 0; b < PB; ++b) {
+      const int f = st * PB + b;
+      if (f < NF) {
+        const int sg = f / KCH, i = f - sg * KCH;
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+          const auto v = __builtin_amdgcn_raw_buffer_load_b128(
+              crs[r], (int)(coff[r] + sg * seg_stride + 256 * i), 0, kCachePolicyNt);
+          q[b][r] = make_uint4(v[0], v[1], v[2], v[3]);
+          if (FMT == MOE_FMT_MXFP4)
+            sc[b][r] = __builtin_amdgcn_raw_buffer_load_b8(
+                srs[r], (int)(soff[r] + sg * seg_sstride + 16 * i), 0, kCachePolicyNt);
+          else
+            sc[b][r] = __builtin_amdgcn_raw_buffer_load_b16(
+                srs[r], (int)(soff[r] + sg * seg_sstride + 32 * i), 0, kCachePolicyNt);
+        }
+      }
+    }
+  }
+  template <class Done>
+  __device__ __forceinline__ void fma(int st, const uint4 (&q)[PB][NR], const uint32_t (&sc)[PB][NR],
+                                      const float* xs, float (&acc)[NR][1], Done& done) const {
+    const int l16 = threadIdx.x & 15;
+#pragma unroll
+    for (int b = 0; b < PB; ++b) {
+      const int f = st * PB + b;
+      if (f < NF) {
+        const int sg = f / KCH, i = f - sg * KCH;
+        chunk_fma1<FMT, NR>(q[b], sc[b], xs, (l16 + 16 * i) * 36, acc);
+        if (i == KCH - 1) {
+          done(sg, acc);
+#pragma unroll
+          for (int r = 0; r < NR; ++r) acc[r][0] = 0.0f;
+        }
+      }
+    }
+  }
+  // all stages; stage 0 may already be loaded into q0
+  template <class Done>
+  __device__ __forceinline__ void run(const float* xs, uint4 (&q0)[PB][NR], uint32_t (&s0)[PB][NR],
+                                      bool stage0_loaded, Done done) const {
+    uint4 q1[PB][NR];
+    uint32_t s1[PB][NR];
+    float acc[NR][1];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) acc[r][0] = 0.0f;
+    if (!stage0_loaded) load(0, q0, s0);
+    // the barriers pin the pipeline: stage t+1's loads are issued just before
+    // stage t is multiplied, never earlier (earlier would need more registers)
+#pragma unroll
+    for (int st = 0; st < NST; ++st) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (st & 1) {
+        if (st + 1 < NST) load(st + 1, q0, s0);
+        __builtin_amdgcn_sched_barrier(0);
+        fma(st, q1, s1, xs, acc, done);
+      } else {
+        if (st + 1 < NST) load(st + 1, q1, s1);
+        __builtin_amdgcn_sched_barrier(0);
+        fma(st, q0, s0, xs, acc, done);
+      }
+    }
+  }
+};
+
+// Gate/up slice: rows b*16*SGU + lg + 16*s (s < SGU) of slot u's expert;
+// h = silu(g) * u goes out as tagged words.
+template <int FMT, int KG, int SGU>
+__device__ void moe1_gate_up_slice(const Moe1Args& a, Moe1Shared& S, int u, int b, uint32_t epoch) {
+  const int e = S.sidx[u];
+  if (e < 0 || e >= a.E) return;                 // an invalid slot contributes nothing
+  const int lg = threadIdx.x >> 4, l16 = threadIdx.x & 15;
+  const int H = a.H, I = a.I;
+  const int B = (FMT == MOE_FMT_MXFP4) ? 32 : 16;
+  const int row0 = b * (kWG1 / 16) * SGU + lg;
+  const uint8_t* rec = a.base + (size_t)e * a.stride;
+  SegStream<FMT, 2, SGU, KG, kGuStage> ss;
+  const uint32_t cbytes = (uint32_t)I * (H / 2), sbytes = (uint32_t)I * (H / B);
+  ss.crs[0] = tensor_view(rec, a.off[MOE_T_GATE_CODES], cbytes);
+  ss.crs[1] = tensor_view(rec, a.off[MOE_T_UP_CODES], cbytes);
+  ss.srs[0] = tensor_view(rec, a.off[MOE_T_GATE_SCALES], sbytes);
+  ss.srs[1] = tensor_view(rec, a.off[MOE_T_UP_SCALES], sbytes);
+  ss.coff[0] = ss.coff[1] = (uint32_t)row0 * (H / 2) + l16 * 16;
+  ss.soff[0] = ss.soff[1] = (uint32_t)row0 * (H / B) + l16 * (32 / B);
+  ss.seg_stride = (kWG1 / 16) * (uint32_t)(H / 2);
+  ss.seg_sstride = (kWG1 / 16) * (uint32_t)(H / B);
+  float gg = 1.0f, gu = 1.0f;
+  if (FMT == MOE_FMT_NVFP4) {
+    const float* g = reinterpret_cast<const float*>(rec + a.off[MOE_T_GLOBALS]);
+    gg = g[0];
+    gu = g[1];
+  }
+  uint64_t* hout = a.th + (size_t)u * I;
+  auto done = [&](int sg, float (&acc)[2][1]) {
+    const float gsum = group16_sum(acc[0][0]);
+    const float usum = group16_sum(acc[1][0]);
+    if (l16 == 0) store_tagged(&hout[row0 + (kWG1 / 16) * sg], epoch, silu(gg * gsum) * (gu * usum));
+  };
+  uint4 q0[kGuStage][2];
+  uint32_t s0[kGuStage][2];
+  ss.run(S.u.xs, q0, s0, false, done);
+}
+
+// Down slice: rows b*R + lg + 16*s (within the block of R = H / workgroups per
+// slot) of slot u's expert, against h_u; the results go out as tagged words,
+// or, for the last slot, to LDS for the combine.
+template <int FMT, int KD, int SDN>
+__device__ void moe1_down_slice(const Moe1Args& a, Moe1Shared& S, int u, int b, int R,
+                                uint32_t epoch) {
+  const int e = S.sidx[u];
+  const bool valid = e >= 0 && e < a.E;
+  const bool combiner = (u == a.k - 1);
+  const int lg = threadIdx.x >> 4, l16 = threadIdx.x & 15;
+  const int H = a.H, I = a.I;
+  const int B = (FMT == MOE_FMT_MXFP4) ? 32 : 16;
+  const int row0 = b * R + lg;
+  if (valid) {
+    const uint8_t* rec = a.base + (size_t)e * a.stride;
+    SegStream<FMT, 1, SDN, KD, kDnStage> ss;
+    // rows past the tensor read zeros (descriptor bounds) and are never stored
+    ss.crs[0] = tensor_view(rec, a.off[MOE_T_DOWN_CODES], (uint32_t)H * (I / 2));
+    ss.srs[0] = tensor_view(rec, a.off[MOE_T_DOWN_SCALES], (uint32_t)H * (I / B));
+    ss.coff[0] = (uint32_t)row0 * (I / 2) + l16 * 16;
+    ss.soff[0] = (uint32_t)row0 * (I / B) + l16 * (32 / B);
+    ss.seg_stride = (kWG1 / 16) * (uint32_t)(I / 2);
+    ss.seg_sstride = (kWG1 / 16) * (uint32_t)(I / B);
+    uint4 q0[kDnStage][1];
+    uint32_t s0[kDnStage][1];
+    ss.load(0, q0, s0);
+    // the first weights are in flight; now fetch this slot's h (polling until
+    // every value carries this call's epoch) into LDS, over the dead x stage
+    __syncthreads();
+    {
+      const __amdgpu_buffer_rsrc_t hv = coherent_view(a.th + (size_t)u * I, (uint32_t)I * 8);
+      constexpr int NP = (KD * 512 / 2 + kWG1 - 1) / kWG1;   // 16-byte pairs per thread
+      for (uint32_t it = 0;; ++it) {
+        bool missing = false;
+        uint4 t[NP];
+#pragma unroll
+        for (int v = 0; v < NP; ++v) {                     // all loads in flight at once
+          const int i = (threadIdx.x + v * kWG1) * 2;
+          t[v] = coherent_ld_u4(hv, (uint32_t)i * 8);      // past the end reads zeros
+        }
+#pragma unroll
+        for (int v = 0; v < NP; ++v) {
+          const int i = (threadIdx.x + v * kWG1) * 2;
+          if (i < I) {
+            missing |= (t[v].y != epoch) | (t[v].w != epoch);
+            *reinterpret_cast<float2*>(&S.u.hs[i + (i >> 5) * 4]) =
+                make_float2(__uint_as_float(t[v].x), __uint_as_float(t[v].z));
+          }
+        }
+        if (!wg_any(missing, &S.flag)) break;
+        if (it == kSpinLimit) {
+          if (threadIdx.x == 0)
+            __hip_atomic_store(&a.ctrl[kCtrlErr], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+      }
+    }
+    float gd = 1.0f;
+    if (FMT == MOE_FMT_NVFP4) gd = reinterpret_cast<const float*>(rec + a.off[MOE_T_GLOBALS])[2];
+    const float wgt = S.sw[u] * gd;
+    auto done = [&](int sg, float (&acc)[1][1]) {
+      const float y = wgt * group16_sum(acc[0][0]);
+      const int rl = lg + (kWG1 / 16) * sg, j = b * R + rl;
+      if (l16 == 0 && rl < R && j < H) {
+        if (combiner) S.ys[rl] = y;
+        else store_tagged(&a.tpart[(size_t)u * H + j], epoch, y);
+      }
+    };
+    ss.run(S.u.hs, q0, s0, true, done);
+  }
+  if (!combiner) return;
+  // the last slot's workgroups add the k slot results of their rows in order
+  __syncthreads();
+  const __amdgpu_buffer_rsrc_t pv = coherent_view(a.tpart, (uint32_t)((size_t)a.k * H * 8));
+  for (int t0 = 0; t0 < R; t0 += kWG1) {
+    const int rl = t0 + threadIdx.x, j = b * R + rl;
+    const bool mine = rl < R && j < H;
+    float acc = 0.0f;
+    for (uint32_t it = 0;; ++it) {
+      bool missing = false;
+      acc = 0.0f;
+      if (mine) {
+        for (int sl = 0; sl < a.k - 1; ++sl) {
+          const int ee = S.sidx[sl];
+          if (ee >= 0 && ee < a.E) {
+            const uint2 t = coherent_ld_u2(pv, (uint32_t)(((size_t)sl * H + j) * 8));
+            missing |= t.y != epoch;
+            acc += __uint_as_float(t.x);
+          }
+        }
+      }
+      if (!wg_any(missing, &S.flag)) break;
+      if (it == kSpinLimit) {
+        if (threadIdx.x == 0)
+          __hip_atomic_store(&a.ctrl[kCtrlErr], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+    if (mine) {
+      if (valid) acc += S.ys[rl];
+      a.out[j] = acc;
+    }
+  }
+}
+
+// The whole layer for one token, under a cooperative launch of kG1
+// workgroups (all resident at once).  Every workgroup has a fixed share of
+// each phase, and every expert has the same size, so the work is balanced
+// whatever the routing (the one-GPU form of slicing every expert across
+// workers, page "Kimi-K3 on the same pod, two engines", section "Reason 1"):
+//   1. router rows e = w, w + G, ...  (four at a time, a half row per wave)
+//   2. the selection: every workgroup reads all E tagged logits and runs the
+//      same top-k on them
+//   3. gate/up: slot u = w / (G/k), 32*SGU rows of I
+//   4. down: the same slot, H / (G/k) rows of H; then the workgroups of the
+//      last slot add the k slot results of their rows in slot order.
+// Hand-offs carry the call's epoch (see above); the polls form a chain
+// router -> selection -> gate/up -> down -> combine, so with every workgroup
+// resident each poll ends, and each is bounded anyway.
+// KG = H/512, KD = I/512 (16-byte chunks per lane per row); SGU, SDN: row
+// segments per 16-lane group in the gate/up and down slices.
+template <int FMT, int KG, int KD, int SGU, int SDN>
+__global__ __launch_bounds__(kWG1, 1) void k_moe1(Moe1Args a) {
+  __shared__ Moe1Shared S;
+  const int tid = threadIdx.x;
+  // x stays in LDS through the gate/up slice
+  for (int i = tid * 4; i < a.H; i += kWG1 * 4)
+    *reinterpret_cast<float4*>(&S.u.xs[i + (i >> 5) * 4]) = *reinterpret_cast<const float4*>(a.x + i);
+  const uint32_t epoch =
+      __hip_atomic_load(&a.ctrl[kCtrlEpoch], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+  __syncthreads();
+  for (int e0 = blockIdx.x; e0 < a.n_router; e0 += 4 * gridDim.x) moe1_router_rows(a, S, e0, epoch);
+  moe1_routing(a, S, epoch, blockIdx.x == 0);
+  const int wpe = gridDim.x / a.k;               // workgroups per slot
+  const int u = blockIdx.x / wpe, b = blockIdx.x - u * wpe;
+  moe1_gate_up_slice<FMT, KG, SGU>(a, S, u, b, epoch);
+  moe1_down_slice<FMT, KD, SDN>(a, S, u, b, a.H / wpe, epoch);
+  // the last workgroup out advances the epoch for the next call
+  if (tid == 0 &&
+      __hip_atomic_fetch_add(&a.ctrl[kCtrlExit], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+          gridDim.x - 1) {
+    __hip_atomic_store(&a.ctrl[kCtrlEpoch], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    reset_ticket(&a.ctrl[kCtrlExit]);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -900,6 +1620,73 @@ moe_status launch_experts(const moe_bank* b, const float* x, int C, int k, const
   return launch_status();
 }
 
+// The batch-1 kernel instances that are built: (format, H, I, k) -> template.
+// Each needs k | kG1, 16 | I*k/kG1 rows per gate/up slice, and kG1/k | H.
+struct Moe1Shape {
+  int H, I, k;
+};
+
+template <int FMT, int KG, int KD, int SGU, int SDN>
+moe_status launch_moe1_kernel(Moe1Args a, hipStream_t st) {
+  static int ok_dev[64] = {0};   // 1: kG1 workgroups fit at once on this device, -1: they do not
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (ok_dev[dev] == 0) {
+    int per_cu = 0;
+    const bool fits = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                          &per_cu, k_moe1<FMT, KG, KD, SGU, SDN>, kWG1, 0) == hipSuccess &&
+                      per_cu * device_cu_count() >= kG1;
+    ok_dev[dev] = fits ? 1 : -1;
+  }
+  if (ok_dev[dev] < 0) return MOE_ERR_UNSUPPORTED;
+  void* args[] = {&a};
+  const hipError_t err = hipLaunchCooperativeKernel(
+      reinterpret_cast<const void*>(k_moe1<FMT, KG, KD, SGU, SDN>), dim3(kG1), dim3(kWG1), args, 0, st);
+  if (err != hipSuccess) {
+    (void)hipGetLastError();
+    return MOE_ERR_UNSUPPORTED;
+  }
+  return MOE_OK;
+}
+
+template <int FMT>
+moe_status launch_moe1_fmt(const Moe1Args& a, hipStream_t st) {
+  // SGU = I*k / (kG1 * 32), SDN = ceil(H*k / (kG1 * 32))
+  if (a.H == 7168 && a.I == 1536 && a.k == 16) return launch_moe1_kernel<FMT, 14, 3, 3, 14>(a, st);
+  if (a.H == 3584 && a.I == 3072 && a.k == 16) return launch_moe1_kernel<FMT, 7, 6, 6, 7>(a, st);
+  if (a.H == 3584 && a.I == 3072 && a.k == 8) return launch_moe1_kernel<FMT, 7, 6, 3, 4>(a, st);
+  return MOE_ERR_UNSUPPORTED;
+}
+
+bool moe1_fits(const moe_bank* b, int C, int k) {
+  if (C != 1) return false;
+  const int H = b->hidden, I = b->inter;
+  const bool built = (H == 7168 && I == 1536 && k == 16) || (H == 3584 && I == 3072 && (k == 16 || k == 8));
+  // the combining slice keeps its R = H / (kG1 / k) rows in LDS, one per thread
+  return built && H / (kG1 / k) <= kWG1;
+}
+
+// MOE_ERR_UNSUPPORTED when the cooperative launch is not possible (the caller
+// then takes the multi-kernel path); nothing has been enqueued in that case.
+moe_status launch_moe1(const moe_bank* b, const float* Wr, const float* x, int k,
+                       const int32_t* idx_in, const float* w_in, int32_t* idx_out, float* w_out,
+                       float* out, uint8_t* ws, const WsLayout& L, hipStream_t st) {
+  Moe1Args a;
+  a.base = static_cast<const uint8_t*>(b->base);
+  a.stride = b->expert_stride;
+  for (int t = 0; t < MOE_NUM_TENSORS; ++t) a.off[t] = b->offset[t];
+  a.E = b->num_experts; a.H = b->hidden; a.I = b->inter; a.k = k;
+  a.x = x; a.Wr = Wr; a.idx_in = idx_in; a.w_in = w_in; a.idx_out = idx_out; a.w_out = w_out;
+  a.tlogits = reinterpret_cast<uint64_t*>(ws + L.tlogits);
+  a.th = reinterpret_cast<uint64_t*>(ws + L.th);
+  a.tpart = reinterpret_cast<uint64_t*>(ws + L.tpart);
+  a.out = out;
+  a.ctrl = reinterpret_cast<uint32_t*>(ws + L.ctrl);
+  a.n_router = Wr ? a.E : 0;
+  return b->format == MOE_FMT_MXFP4 ? launch_moe1_fmt<MOE_FMT_MXFP4>(a, st)
+                                    : launch_moe1_fmt<MOE_FMT_NVFP4>(a, st);
+}
+
 bool tokens_ok(int C) { return C >= 1 && C <= MOE_MAX_DECODE_TOKENS; }
 bool topk_ok(int k, int E) { return k >= 1 && k <= MOE_MAX_TOPK && k <= E; }
 
@@ -988,6 +1775,11 @@ moe_status moe_expert_fwd(const moe_bank* bank, const float* x, int32_t C, int32
   if (ws_bytes < L.total || !aligned(ws, 256)) return MOE_ERR_WORKSPACE;
   uint8_t* w8 = static_cast<uint8_t*>(ws);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (moe1_fits(bank, C, k)) {
+    const moe_status m = launch_moe1(bank, nullptr, x, k, topk_idx, topk_w, nullptr, nullptr, out,
+                                     w8, L, st);
+    if (m != MOE_ERR_UNSUPPORTED) return m;
+  }
   hipLaunchKernelGGL(k_dispatch, dim3(1), dim3(kWG), 0, st, topk_idx,
                      reinterpret_cast<int32_t*>(w8 + L.disp), C, k, bank->num_experts);
   if ((s = launch_status()) != MOE_OK) return s;
@@ -1009,6 +1801,10 @@ moe_status moe_layer_fwd(const moe_bank* bank, const float* w_router, const floa
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   int32_t* idx = topk_idx_out ? topk_idx_out : reinterpret_cast<int32_t*>(w8 + L.idx);
   float* w = topk_w_out ? topk_w_out : reinterpret_cast<float*>(w8 + L.w);
+  if (moe1_fits(bank, C, k)) {
+    const moe_status m = launch_moe1(bank, w_router, x, k, nullptr, nullptr, idx, w, out, w8, L, st);
+    if (m != MOE_ERR_UNSUPPORTED) return m;
+  }
   s = launch_route(x, w_router, nullptr, nullptr, C, bank->hidden, bank->num_experts, k, idx, w,
                    reinterpret_cast<int32_t*>(w8 + L.disp), w8, L, st);
   if (s != MOE_OK) return s;

@@ -323,3 +323,26 @@ def test_workspace_reuse_across_shapes():
         ref = oracle.layer(spec, Wr, x, wl.k)
         assert np.array_equal(idx.cpu().numpy(), ref["idx"])
         assert_close(out.cpu().numpy(), ref["out"], f"reuse C={C}")
+
+
+@pytest.mark.parametrize("name,C", [("w50_k16", 1), ("w50_c7_k16", 7), ("k3_stack", 1)])
+def test_layer_repeat_bit_identical(name, C):
+    """60 back-to-back calls on one stream give bit-identical outputs: the
+    cross-workgroup hand-offs (router partial sums, per-slot down outputs)
+    are complete before the last workgroup sums them."""
+    say(f"[layer] repeat x60 {name} C={C}")
+    wl = synth.WORKLOADS[name]
+    spec = wl.bank(0)
+    bank = cached_bank(spec)
+    Wr, x = synth.layer_inputs(wl, 0, C=C, pool=3)
+    ws = _ws(wl.E, wl.H, wl.I, wl.k, C)
+    Wr_d, x_d = to_dev(Wr), to_dev(x)
+    outs = torch.empty((60, C, wl.H), dtype=torch.float32, device="cuda")
+    idxs = torch.empty((60, C, wl.k), dtype=torch.int32, device="cuda")
+    for i in range(60):
+        rf().moe_layer_fwd(bank, Wr_d, x_d, C, wl.k, outs[i], idxs[i], None, ws)
+    torch.cuda.synchronize()
+    o = outs.cpu().numpy().view(np.uint32)
+    ix = idxs.cpu().numpy()
+    assert all(np.array_equal(o[0], o[i]) for i in range(60))
+    assert all(np.array_equal(ix[0], ix[i]) for i in range(60))
