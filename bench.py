@@ -8,9 +8,11 @@ natural router (uniform routing).  One step = one token through the 12 layers,
 16 pre-drawn tokens per layer, so consecutive steps select different experts.
 
 Prints one JSON line: the metric (MoE-layer decode us/token, with achieved HBM
-GB/s on selected-expert bytes), a roofline object for the dominant kernel work
-(the expert weight stream, timed with HIP events around moe_expert_fwd on the
-stream it runs on) and the CPU oracle timed on a bounded sample.
+GB/s on selected-expert bytes), a roofline object for the kernel that runs the
+whole layer for one token (k_moe1: one launch per moe_layer_fwd call; its
+algorithmic bytes are the router weights plus the selected experts' weights,
+timed with HIP events on the stream it is launched on) and the CPU oracle timed
+on a bounded sample.
 """
 from __future__ import annotations
 
@@ -44,6 +46,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-layers", type=int, default=1,
                    help="layer-tokens of the workload the CPU oracle is timed on")
+    p.add_argument("--layer-only", action="store_true",
+                   help="time only the whole-layer step (no expert-only / route-only loops), "
+                        "so a kernel trace holds only the layer kernel's launches")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run a plain 2 GiB device copy (HBM counter calibration)")
     return p.parse_args()
@@ -58,6 +63,29 @@ def calibrate_copy():
         dst.copy_(src)
     torch.cuda.synchronize()
     log(f"copied {n} bytes x 3")
+
+
+KERNEL_SRC = os.path.join(ROOT, "routed_expert_fp4_amd", "csrc", "routed_fp4.hip")
+COUNTERS = os.path.join(ROOT, "profiles", "k_moe1_k3_stack_nvfp4_hbm_counters.md")
+
+
+def measured_traffic():
+    """HBM bytes per layer-kernel launch from the committed counter summary
+    (FETCH_SIZE + WRITE_SIZE, each scaled by a plain copy's reading), or None
+    when the kernel source has changed since the counters were taken."""
+    import hashlib
+    import re
+    try:
+        text = open(COUNTERS).read()
+    except OSError:
+        return None
+    h = re.search(r"source-sha256: ([0-9a-f]{64})", text)
+    t = re.search(r"traffic_bytes_per_launch: (\d+)", text)
+    if not h or not t:
+        return None
+    if hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest() != h.group(1):
+        return None
+    return int(t.group(1))
 
 
 def expert_bytes(spec) -> int:
@@ -202,8 +230,8 @@ def main():
         torch.cuda.synchronize()
         return a.elapsed_time(b) / (n * wl.layers) * 1000.0     # us per layer call
 
-    us_expert = timed(expert_step, args.steps)
-    us_route = timed(route_step, args.steps)
+    us_expert = timed(expert_step, args.steps) if not args.layer_only else float("nan")
+    us_route = timed(route_step, args.steps) if not args.layer_only else float("nan")
     # distinct experts per call (C = 1: always k)
     uniq = np.mean([len(np.unique(idx[l][j].cpu().numpy())) for l in range(wl.layers)
                     for j in range(POOL)])
@@ -211,7 +239,10 @@ def main():
     sel_bytes = uniq * expert_bytes(spec0)
     router_bytes = wl.E * wl.H * 4
     gbps_layer = sel_bytes / (us_layer * 1e-6) / 1e9
-    gbps_expert = sel_bytes / (us_expert * 1e-6) / 1e9
+    # the layer kernel's algorithmic bytes: router weights + selected experts
+    # (+ x in, y out: 2 * H * 4, negligible but counted)
+    alg_bytes = router_bytes + sel_bytes + 2 * wl.H * 4
+    gbps_kernel = alg_bytes / (us_layer * 1e-6) / 1e9
 
     result = {
         "metric": METRIC,
@@ -237,13 +268,14 @@ def main():
         "tokens_per_s": round(1000.0 / ms_step, 2),
         "selected_expert_bytes_per_layer": int(sel_bytes),
         "router_bytes_per_layer": router_bytes,
-        "us_per_layer_route": round(us_route, 3),
-        "us_per_layer_experts": round(us_expert, 3),
-        "roofline": {"bound": "hbm", "achieved": round(gbps_expert, 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(gbps_expert / HBM_PEAK_GBPS, 4), "traffic": None,
-                     "kernel": "expert weight stream: moe_expert_fwd per layer call "
-                               "(k_dispatch + k_gate_up + k_down + k_zero_uncovered), "
-                               "16 x 18,579,468 selected-expert bytes per launch set"},
+        "us_per_layer_route": None if args.layer_only else round(us_route, 3),
+        "us_per_layer_experts": None if args.layer_only else round(us_expert, 3),
+        "roofline": {"bound": "hbm", "achieved": round(gbps_kernel, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(gbps_kernel / HBM_PEAK_GBPS, 4),
+                     "traffic": measured_traffic() if wl.name == "k3_stack" else None,
+                     "kernel": "k_moe1 (whole layer, one launch per moe_layer_fwd call)",
+                     "bytes_per_launch": int(alg_bytes),
+                     "us_per_launch": round(us_layer, 3)},
         "wall_s_timed": round(wall, 3),
     }
     if not args.no_cpu_baseline:

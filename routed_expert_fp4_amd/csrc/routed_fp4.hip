@@ -843,7 +843,7 @@ __global__ void k_zero_uncovered(ExpArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Batch-1 decode: the whole layer as one cooperative kernel
+// Batch-1 decode: the whole layer as one kernel of co-resident workgroups
 // ---------------------------------------------------------------------------
 // Hand-offs between workgroups carry the call's epoch: a producer writes
 // (epoch, value) as one 64-bit agent-coherent store and moves on; a consumer
@@ -915,7 +915,10 @@ struct Moe1Shared {
     float xs[kMaxH1 + kMaxH1 / 8];   // x, padded 4 floats per 32 (router, gate/up)
     float hs[kMaxI1 + kMaxI1 / 8];   // h of the slot (down)
   } u;
-  TopkShared topk;
+  uint64_t cand_key[64];          // the selection's candidates (wave 0)
+  float cand_l[64];
+  int32_t sel_e[MOE_MAX_TOPK];     // the selection in rank order
+  float sel_l[MOE_MAX_TOPK];
   float ys[kWG1];                  // the combining slice's own rows (R <= kWG1)
   int32_t sidx[MOE_MAX_TOPK];
   float sw[MOE_MAX_TOPK];
@@ -934,34 +937,45 @@ __device__ __forceinline__ bool wg_any(bool v, int* s_flag) {
 // Router rows e0, e0 + kG1, e0 + 2*kG1, e0 + 3*kG1 (those below E) at once:
 // wave w takes half (w & 1) of row w >> 1, so every weight load of the four
 // rows is in flight together; the two halves are added in a fixed order and
-// the logit is written, tagged, to every replica.
-__device__ void moe1_router_rows(const Moe1Args& a, Moe1Shared& S, int e0, uint32_t epoch) {
+// the logit is written, tagged, to every replica.  The loads are issued
+// first (moe1_router_load) so they can be in flight while x is staged.
+constexpr int kRouterRU = kMaxH1 / 2 / 4 / 64;     // float4 loads per lane (max)
+
+__device__ __forceinline__ void moe1_router_load(const Moe1Args& a, int e0, float4 (&wv)[kRouterRU]) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int r = wave >> 1, half = wave & 1;
   const int e = e0 + r * kG1;
   const int q = a.H / 2;                          // this wave's half of K
-  constexpr int RU = kMaxH1 / 2 / 4 / 64;         // float4 loads per lane (max)
-  float acc = 0.0f;
+#pragma unroll
+  for (int u = 0; u < kRouterRU; ++u) wv[u] = make_float4(0.f, 0.f, 0.f, 0.f);
   if (e < a.E) {
     const __amdgpu_buffer_rsrc_t wr =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(a.Wr + (size_t)e * a.H), (short)0,
                                           a.H * 4, 0x00020000);
     const uint32_t woff = (uint32_t)(half * q + lane * 4) * 4;
-    float4 wv[RU];
 #pragma unroll
-    for (int u = 0; u < RU; ++u) {
+    for (int u = 0; u < kRouterRU; ++u) {
       const int c = (lane + 64 * u) * 4;
       if (c < q) {
         const auto v = __builtin_amdgcn_raw_buffer_load_b128(wr, (int)(woff + 1024 * u), 0,
                                                              kCachePolicyNt);
         wv[u] = make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]),
                             __uint_as_float(v[3]));
-      } else {
-        wv[u] = make_float4(0.f, 0.f, 0.f, 0.f);
       }
     }
+  }
+}
+
+__device__ __forceinline__ void moe1_router_finish(const Moe1Args& a, Moe1Shared& S, int e0,
+                                   const float4 (&wv)[kRouterRU], uint32_t epoch) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r = wave >> 1, half = wave & 1;
+  const int e = e0 + r * kG1;
+  const int q = a.H / 2;
+  float acc = 0.0f;
+  if (e < a.E) {
 #pragma unroll
-    for (int u = 0; u < RU; ++u) {
+    for (int u = 0; u < kRouterRU; ++u) {
       const int c = (lane + 64 * u) * 4;
       if (c < q) {
         const int col = half * q + c;
@@ -982,67 +996,147 @@ __device__ void moe1_router_rows(const Moe1Args& a, Moe1Shared& S, int e0, uint3
   __syncthreads();
 }
 
+// Selection key of expert e with logit l: larger is better; equal logits go
+// to the lower index; 0 marks an empty entry (every real key is above it).
+__device__ __forceinline__ uint64_t sel_key(float l, int e) {
+  return ((uint64_t)logit_key(l) << 32) | (uint64_t)(~(uint32_t)e);
+}
+
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
+  const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, m, 64);
+  const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), m, 64);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Orders LDS accesses of one wave (a compiler fence only: a wave's LDS
+// operations complete in issue order).
+__device__ __forceinline__ void wave_lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Exact top-k of the entries one wave holds, NPL per lane (key ck[i], logit
+// lv[i]; empty entries have key 0), k <= 32 and at least k entries non-empty.
+// Writes the winners' experts and logits, best first, to S.sel_e / S.sel_l.
+//
+// A threshold first: T = the k-th largest of the 64 lane maxima.  The k lanes
+// whose maxima are >= T hold k entries >= T, so the top k are all >= T.  The
+// entries >= T (usually a few more than k) are gathered one per lane, and each
+// one's rank is the number of gathered keys above it.  When more than 64
+// entries pass the threshold (heavily clustered winners), k rounds of "take
+// the wave's best remaining entry" do the job instead.
+template <int NPL>
+__device__ void wave_select(uint64_t (&ck)[NPL], const float (&lv)[NPL], int k, Moe1Shared& S) {
+  const int lane = threadIdx.x & 63;
+  uint64_t m = 0;
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) m = ck[i] > m ? ck[i] : m;
+  int r = 0;                                   // rank of this lane's maximum
+  for (int j = 0; j < 64; ++j) r += readlane_u64(m, j) > m ? 1 : 0;
+  // non-empty maxima are distinct, so exactly one lane has rank k - 1
+  const unsigned long long at = __ballot(r == k - 1);
+  const uint64_t T = at ? readlane_u64(m, __ffsll((long long)at) - 1) : 0;
+  int n = 0;
+  unsigned long long pass[NPL];
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) {
+    pass[i] = __ballot(ck[i] >= T && ck[i] != 0);
+    n += __popcll(pass[i]);
+  }
+  if (n <= 64) {
+    int base = 0;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+      if ((pass[i] >> lane) & 1ull) {
+        const int pos = base + __popcll(pass[i] & ((1ull << lane) - 1ull));
+        S.cand_key[pos] = ck[i];
+        S.cand_l[pos] = lv[i];
+      }
+      base += __popcll(pass[i]);
+    }
+    wave_lds_fence();
+    const uint64_t mine = lane < n ? S.cand_key[lane] : 0;
+    const float ml = lane < n ? S.cand_l[lane] : 0.0f;
+    int rk = 0;
+    for (int j = 0; j < n; ++j) rk += readlane_u64(mine, j) > mine ? 1 : 0;
+    if (lane < n && rk < k) {
+      S.sel_e[rk] = (int32_t)~(uint32_t)mine;
+      S.sel_l[rk] = ml;
+    }
+  } else {
+    for (int s = 0; s < k; ++s) {
+      uint64_t b = 0;
+#pragma unroll
+      for (int i = 0; i < NPL; ++i) b = ck[i] > b ? ck[i] : b;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const uint64_t o = shfl_xor_u64(b, d);
+        b = o > b ? o : b;
+      }
+#pragma unroll
+      for (int i = 0; i < NPL; ++i) {
+        if (b != 0 && ck[i] == b) {          // one entry of one lane
+          S.sel_e[s] = (int32_t)~(uint32_t)b;
+          S.sel_l[s] = lv[i];
+          ck[i] = 0;
+        }
+      }
+    }
+  }
+  wave_lds_fence();
+}
+
 // The selection, computed by every workgroup for itself from the tagged
-// logits (or taken from the caller when the selection is given).
+// logits (or taken from the caller when the selection is given).  Wave 0
+// polls one replica of the logits (expert lane + 64 i in lane, slot i) and
+// selects; the other waves wait at the closing barrier.
 __device__ void moe1_routing(const Moe1Args& a, Moe1Shared& S, uint32_t epoch, bool writer) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int k = a.k;
+  constexpr int NPL = MOE_MAX_EXPERTS / 64;
   if (a.Wr) {
-    // wave w holds experts w*256 + lane + 64*i, i < 4
-    uint32_t key[4], ix[4];
-    float lv[4];
-    const __amdgpu_buffer_rsrc_t lr = coherent_view(
-        a.tlogits + (size_t)(blockIdx.x % kLogitCopies) * a.E, (uint32_t)a.E * 8);
-    for (uint32_t it = 0;; ++it) {
-      bool missing = false;
-      uint2 t[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) t[i] = coherent_ld_u2(lr, (uint32_t)(wave * 256 + lane + 64 * i) * 8);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int e = wave * 256 + lane + 64 * i;
-        if (wave < 4 && e < a.E) {
-          missing |= t[i].y != epoch;
-          lv[i] = __uint_as_float(t[i].x);
-          key[i] = logit_key(lv[i]);
-          ix[i] = (uint32_t)e;
-        } else {
-          lv[i] = 0.0f;
-          key[i] = 0u;
-          ix[i] = 0xFFFFu;
-        }
-      }
-      if (!wg_any(missing, &S.flag)) break;
-      if (it == kSpinLimit) {
-        if (threadIdx.x == 0)
-          __hip_atomic_store(&a.ctrl[kCtrlErr], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        break;
-      }
-      __builtin_amdgcn_s_sleep(2);
-    }
-    TopkShared& T = S.topk;
-    if (wave < 4) wave_tournament<4>(key, ix, lv, k, T.sel_key[wave], T.sel_e[wave], T.sel_l[wave]);
-    __syncthreads();
     if (wave == 0) {
-      // merge the 4 waves' k best (4k <= 128 entries, two per lane)
-      uint32_t mk[2], mi[2];
-      float ml[2];
+      uint64_t ck[NPL];
+      float lv[NPL];
+      const __amdgpu_buffer_rsrc_t lr = coherent_view(
+          a.tlogits + (size_t)(blockIdx.x % kLogitCopies) * a.E, (uint32_t)a.E * 8);
+      for (uint32_t it = 0;; ++it) {
+        uint2 t[NPL];
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int c = lane + 64 * h;          // candidate c: wave c / k, rank c % k
-        const int w = c / k, r = c - w * k;
-        if (w < 4) {
-          mk[h] = T.sel_key[w][r]; mi[h] = (uint32_t)T.sel_e[w][r]; ml[h] = T.sel_l[w][r];
-        } else {
-          mk[h] = 0u; mi[h] = 0xFFFFu; ml[h] = 0.0f;
+        for (int i = 0; i < NPL; ++i)
+          if (lane + 64 * i < a.E) t[i] = coherent_ld_u2(lr, (uint32_t)(lane + 64 * i) * 8);
+        bool missing = false;
+#pragma unroll
+        for (int i = 0; i < NPL; ++i) {
+          const int e = lane + 64 * i;
+          if (e < a.E) {
+            missing |= t[i].y != epoch;
+            lv[i] = __uint_as_float(t[i].x);
+            ck[i] = sel_key(lv[i], e);
+          } else {
+            lv[i] = 0.0f;
+            ck[i] = 0;
+          }
         }
+        if (__ballot(missing) == 0ull) break;
+        if (it == kSpinLimit) {
+          if (lane == 0)
+            __hip_atomic_store(&a.ctrl[kCtrlErr], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
       }
-      // (reading all of sel_* before the merge writes its results elsewhere)
-      wave_tournament<2>(mk, mi, ml, k, T.hist[0], T.sorted_e, T.sorted_l[0]);
-      const float l = (lane < k) ? T.sorted_l[0][lane] : 0.0f;
+      wave_select<NPL>(ck, lv, k, S);
+      const float l = lane < k ? S.sel_l[lane] : 0.0f;
       const float w = route_weight(l, lane, k);
       if (lane < k) {
-        const int e = T.sorted_e[lane];
+        const int e = S.sel_e[lane];
         S.sidx[lane] = e;
         S.sw[lane] = w;
         if (writer && a.idx_out) a.idx_out[lane] = e;
@@ -1093,75 +1187,6 @@ __device__ __forceinline__ void chunk_fma1(const uint4 (&q)[NR], const uint32_t 
     __builtin_amdgcn_sched_barrier(0);
   }
 }
-
-// Software-pipelined weight stream: lane l16 of a 16-lane group owns chunks
-// c = l16 + 16*i (i < KCH) of each of NR rows; the chunks go in stages of PB,
-// and the loads of stage s+1 are in flight while stage s is multiplied.  KCH
-// is a compile-time constant, so the whole stream is straight-line code.
-// The loads are buffer loads: one descriptor per tensor (scalar registers),
-// one 32-bit offset per row, and the chunk stride in the instruction's
-// immediate offset, so no per-chunk 64-bit address is ever materialised.
-template <int FMT, int NR, int KCH, int PB>
-struct RowStream {
-  static constexpr int NST = (KCH + PB - 1) / PB;
-  __amdgpu_buffer_rsrc_t crs[NR];   // code tensor of row r
-  __amdgpu_buffer_rsrc_t srs[NR];   // scale tensor of row r
-  uint32_t coff[NR];                // byte offset of (row r, chunk l16) in crs[r]
-  uint32_t soff[NR];                // byte offset of its scale byte(s) in srs[r]
-  __device__ __forceinline__ void load(int st, uint4 (&q)[PB][NR], uint32_t (&sc)[PB][NR]) const {
-#pragma unroll
-    for (int b = 0; b < PB; ++b) {
-      const int i = st * PB + b;
-      if (i < KCH) {
-#pragma unroll
-        for (int r = 0; r < NR; ++r) {
-          const auto v = __builtin_amdgcn_raw_buffer_load_b128(crs[r], (int)(coff[r] + 256 * i), 0,
-                                                               kCachePolicyNt);
-          q[b][r] = make_uint4(v[0], v[1], v[2], v[3]);
-          if (FMT == MOE_FMT_MXFP4)
-            sc[b][r] = __builtin_amdgcn_raw_buffer_load_b8(srs[r], (int)(soff[r] + 16 * i), 0,
-                                                          kCachePolicyNt);
-          else
-            sc[b][r] = __builtin_amdgcn_raw_buffer_load_b16(srs[r], (int)(soff[r] + 32 * i), 0,
-                                                           kCachePolicyNt);
-        }
-      }
-    }
-  }
-  __device__ __forceinline__ void fma(int st, const uint4 (&q)[PB][NR], const uint32_t (&sc)[PB][NR],
-                                      const float* xs, float (&acc)[NR][1]) const {
-    const int l16 = threadIdx.x & 15;
-#pragma unroll
-    for (int b = 0; b < PB; ++b) {
-      if (st * PB + b < KCH) {
-        const int c = l16 + 16 * (st * PB + b);
-        chunk_fma1<FMT, NR>(q[b], sc[b], xs, c * 36, acc);
-      }
-    }
-  }
-  // all stages; stage 0 may already be loaded into q0
-  __device__ __forceinline__ void run(const float* xs, float (&acc)[NR][1], uint4 (&q0)[PB][NR],
-                                      uint32_t (&s0)[PB][NR], bool stage0_loaded) const {
-    uint4 q1[PB][NR];
-    uint32_t s1[PB][NR];
-    if (!stage0_loaded) load(0, q0, s0);
-    // the barriers pin the pipeline: stage s+1's loads are issued just before
-    // stage s is multiplied, never earlier (earlier would need more registers)
-#pragma unroll
-    for (int st = 0; st < NST; ++st) {
-      __builtin_amdgcn_sched_barrier(0);
-      if (st & 1) {
-        if (st + 1 < NST) load(st + 1, q0, s0);
-        __builtin_amdgcn_sched_barrier(0);
-        fma(st, q1, s1, xs, acc);
-      } else {
-        if (st + 1 < NST) load(st + 1, q1, s1);
-        __builtin_amdgcn_sched_barrier(0);
-        fma(st, q0, s0, xs, acc);
-      }
-    }
-  }
-};
 
 // One tensor of one expert as a buffer descriptor.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t tensor_view(const uint8_t* rec, int64_t off,
@@ -1295,7 +1320,7 @@ __device__ void moe1_gate_up_slice(const Moe1Args& a, Moe1Shared& S, int u, int 
 // Down slice: rows b*R + lg + 16*s (within the block of R = H / workgroups per
 // slot) of slot u's expert, against h_u; the results go out as tagged words,
 // or, for the last slot, to LDS for the combine.
-template <int FMT, int KD, int SDN>
+template <int FMT, int KD, int SDN, int KT>
 __device__ void moe1_down_slice(const Moe1Args& a, Moe1Shared& S, int u, int b, int R,
                                 uint32_t epoch) {
   const int e = S.sidx[u];
@@ -1365,8 +1390,9 @@ __device__ void moe1_down_slice(const Moe1Args& a, Moe1Shared& S, int u, int b, 
   }
   if (!combiner) return;
   // the last slot's workgroups add the k slot results of their rows in order
+  // (all k - 1 loads of a row in flight at once)
   __syncthreads();
-  const __amdgpu_buffer_rsrc_t pv = coherent_view(a.tpart, (uint32_t)((size_t)a.k * H * 8));
+  const __amdgpu_buffer_rsrc_t pv = coherent_view(a.tpart, (uint32_t)((size_t)KT * H * 8));
   for (int t0 = 0; t0 < R; t0 += kWG1) {
     const int rl = t0 + threadIdx.x, j = b * R + rl;
     const bool mine = rl < R && j < H;
@@ -1375,12 +1401,15 @@ __device__ void moe1_down_slice(const Moe1Args& a, Moe1Shared& S, int u, int b, 
       bool missing = false;
       acc = 0.0f;
       if (mine) {
-        for (int sl = 0; sl < a.k - 1; ++sl) {
+        uint2 t[KT - 1];
+#pragma unroll
+        for (int sl = 0; sl < KT - 1; ++sl) t[sl] = coherent_ld_u2(pv, (uint32_t)(((size_t)sl * H + j) * 8));
+#pragma unroll
+        for (int sl = 0; sl < KT - 1; ++sl) {
           const int ee = S.sidx[sl];
           if (ee >= 0 && ee < a.E) {
-            const uint2 t = coherent_ld_u2(pv, (uint32_t)(((size_t)sl * H + j) * 8));
-            missing |= t.y != epoch;
-            acc += __uint_as_float(t.x);
+            missing |= t[sl].y != epoch;
+            acc += __uint_as_float(t[sl].x);
           }
         }
       }
@@ -1415,22 +1444,28 @@ __device__ void moe1_down_slice(const Moe1Args& a, Moe1Shared& S, int u, int b, 
 // resident each poll ends, and each is bounded anyway.
 // KG = H/512, KD = I/512 (16-byte chunks per lane per row); SGU, SDN: row
 // segments per 16-lane group in the gate/up and down slices.
-template <int FMT, int KG, int KD, int SGU, int SDN>
+template <int FMT, int KG, int KD, int SGU, int SDN, int KT>
 __global__ __launch_bounds__(kWG1, 1) void k_moe1(Moe1Args a) {
   __shared__ Moe1Shared S;
   const int tid = threadIdx.x;
+  float4 wv[kRouterRU];
+  int e0 = blockIdx.x;
+  if (e0 < a.n_router) moe1_router_load(a, e0, wv);     // in flight while x is staged
   // x stays in LDS through the gate/up slice
   for (int i = tid * 4; i < a.H; i += kWG1 * 4)
     *reinterpret_cast<float4*>(&S.u.xs[i + (i >> 5) * 4]) = *reinterpret_cast<const float4*>(a.x + i);
   const uint32_t epoch =
       __hip_atomic_load(&a.ctrl[kCtrlEpoch], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
   __syncthreads();
-  for (int e0 = blockIdx.x; e0 < a.n_router; e0 += 4 * gridDim.x) moe1_router_rows(a, S, e0, epoch);
+  for (; e0 < a.n_router; e0 += 4 * gridDim.x) {
+    if (e0 != (int)blockIdx.x) moe1_router_load(a, e0, wv);
+    moe1_router_finish(a, S, e0, wv, epoch);
+  }
   moe1_routing(a, S, epoch, blockIdx.x == 0);
   const int wpe = gridDim.x / a.k;               // workgroups per slot
   const int u = blockIdx.x / wpe, b = blockIdx.x - u * wpe;
   moe1_gate_up_slice<FMT, KG, SGU>(a, S, u, b, epoch);
-  moe1_down_slice<FMT, KD, SDN>(a, S, u, b, a.H / wpe, epoch);
+  moe1_down_slice<FMT, KD, SDN, KT>(a, S, u, b, a.H / wpe, epoch);
   // the last workgroup out advances the epoch for the next call
   if (tid == 0 &&
       __hip_atomic_fetch_add(&a.ctrl[kCtrlExit], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
@@ -1626,7 +1661,7 @@ struct Moe1Shape {
   int H, I, k;
 };
 
-template <int FMT, int KG, int KD, int SGU, int SDN>
+template <int FMT, int KG, int KD, int SGU, int SDN, int KT>
 moe_status launch_moe1_kernel(Moe1Args a, hipStream_t st) {
   static int ok_dev[64] = {0};   // 1: kG1 workgroups fit at once on this device, -1: they do not
   int dev = 0;
@@ -1634,27 +1669,29 @@ moe_status launch_moe1_kernel(Moe1Args a, hipStream_t st) {
   if (ok_dev[dev] == 0) {
     int per_cu = 0;
     const bool fits = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                          &per_cu, k_moe1<FMT, KG, KD, SGU, SDN>, kWG1, 0) == hipSuccess &&
+                          &per_cu, k_moe1<FMT, KG, KD, SGU, SDN, KT>, kWG1, 0) == hipSuccess &&
                       per_cu * device_cu_count() >= kG1;
     ok_dev[dev] = fits ? 1 : -1;
   }
   if (ok_dev[dev] < 0) return MOE_ERR_UNSUPPORTED;
-  void* args[] = {&a};
-  const hipError_t err = hipLaunchCooperativeKernel(
-      reinterpret_cast<const void*>(k_moe1<FMT, KG, KD, SGU, SDN>), dim3(kG1), dim3(kWG1), args, 0, st);
-  if (err != hipSuccess) {
-    (void)hipGetLastError();
-    return MOE_ERR_UNSUPPORTED;
-  }
+  // A plain launch: with at most one workgroup per CU and kG1 <= the CUs
+  // that can hold one, every workgroup is resident once the stream's earlier
+  // work has drained, so every wait ends.  (The cooperative launch API gives
+  // the same guarantee but costs about 17 us more per call on this stack.)
+  // Should other work hold CUs indefinitely, the bounded waits give up and set
+  // the workspace's error word instead of hanging.
+  hipLaunchKernelGGL((k_moe1<FMT, KG, KD, SGU, SDN, KT>), dim3(kG1), dim3(kWG1), 0, st, a);
+  const hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return MOE_ERR_DEVICE;
   return MOE_OK;
 }
 
 template <int FMT>
 moe_status launch_moe1_fmt(const Moe1Args& a, hipStream_t st) {
   // SGU = I*k / (kG1 * 32), SDN = ceil(H*k / (kG1 * 32))
-  if (a.H == 7168 && a.I == 1536 && a.k == 16) return launch_moe1_kernel<FMT, 14, 3, 3, 14>(a, st);
-  if (a.H == 3584 && a.I == 3072 && a.k == 16) return launch_moe1_kernel<FMT, 7, 6, 6, 7>(a, st);
-  if (a.H == 3584 && a.I == 3072 && a.k == 8) return launch_moe1_kernel<FMT, 7, 6, 3, 4>(a, st);
+  if (a.H == 7168 && a.I == 1536 && a.k == 16) return launch_moe1_kernel<FMT, 14, 3, 3, 14, 16>(a, st);
+  if (a.H == 3584 && a.I == 3072 && a.k == 16) return launch_moe1_kernel<FMT, 7, 6, 6, 7, 16>(a, st);
+  if (a.H == 3584 && a.I == 3072 && a.k == 8) return launch_moe1_kernel<FMT, 7, 6, 3, 4, 8>(a, st);
   return MOE_ERR_UNSUPPORTED;
 }
 
@@ -1666,8 +1703,9 @@ bool moe1_fits(const moe_bank* b, int C, int k) {
   return built && H / (kG1 / k) <= kWG1;
 }
 
-// MOE_ERR_UNSUPPORTED when the cooperative launch is not possible (the caller
-// then takes the multi-kernel path); nothing has been enqueued in that case.
+// MOE_ERR_UNSUPPORTED when the device cannot hold all kG1 workgroups at once
+// (the caller then takes the multi-kernel path); nothing has been enqueued in
+// that case.
 moe_status launch_moe1(const moe_bank* b, const float* Wr, const float* x, int k,
                        const int32_t* idx_in, const float* w_in, int32_t* idx_out, float* w_out,
                        float* out, uint8_t* ws, const WsLayout& L, hipStream_t st) {
