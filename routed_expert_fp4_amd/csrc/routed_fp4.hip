@@ -3,7 +3,13 @@
 // One MoE layer (the MUL_MAT_ID of page "Kimi-K3 on 2x A40 -- measured
 // findings", section "Why the placement experiments all looked the same"; the
 // router -> top-k -> selected experts -> sum structure of page "SparkInfer-K3",
-// section "How the TP module works") runs as three kernels on one stream:
+// section "How the TP module works") runs one of two ways.
+//
+// One token (C = 1) on a built shape: k_moe1, the whole layer in one launch
+// of co-resident workgroups that hand results to one another through
+// epoch-tagged words (see "Batch-1 decode" below).
+//
+// Otherwise (C = 2..16, or other shapes) three kernels on one stream:
 //
 //   k_route    router mat-vec streamed across all CUs (split-K partial sums);
 //              the last workgroup to finish (atomic ticket) adds the partials
