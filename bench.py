@@ -73,19 +73,30 @@ def measured_traffic():
     """HBM bytes per layer-kernel launch from the committed counter summary
     (FETCH_SIZE + WRITE_SIZE, each scaled by a plain copy's reading), or None
     when the kernel source has changed since the counters were taken."""
-    import hashlib
     import re
     try:
         text = open(COUNTERS).read()
     except OSError:
         return None
-    h = re.search(r"source-sha256: ([0-9a-f]{64})", text)
+    h = re.search(r"code-sha256 [^:]*: ([0-9a-f]{64})", text)
     t = re.search(r"traffic_bytes_per_launch: (\d+)", text)
     if not h or not t:
         return None
-    if hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest() != h.group(1):
+    if code_sha256(KERNEL_SRC) != h.group(1):
         return None
     return int(t.group(1))
+
+
+def code_sha256(path: str) -> str:
+    """sha256 of a C/HIP source with comments and blank space removed, so an
+    edit to comments alone does not void measurements of the same code."""
+    import hashlib
+    import re
+    text = open(path).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    text = "\n".join(line.strip() for line in text.splitlines() if line.strip())
+    return hashlib.sha256(text.encode()).hexdigest()
 
 
 def expert_bytes(spec) -> int:
