@@ -42,7 +42,10 @@ def parse():
     p.add_argument("--steps", type=int, default=100)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="k3_stack",
-                   help="k3_stack (uniform routing) or k3_stack_zipf (Zipf s=1.2)")
+                   choices=["k3_stack", "k3_stack_zipf", "w50_k16", "w50_k8", "w50_c7_k8",
+                            "w50_c7_k16", "tiny"],
+                   help="k3_stack (the headline: 12 layers, uniform routing), k3_stack_zipf "
+                        "(Zipf s=1.2), or one of the single-layer decode workloads")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-layers", type=int, default=1,
                    help="layer-tokens of the workload the CPU oracle is timed on")
@@ -104,39 +107,43 @@ def expert_bytes(spec) -> int:
 
 
 def cpu_baseline(wl, layers: int):
-    """The oracle as it is, on `layers` layer-tokens of the workload; input
-    regeneration (the synthetic bank bytes) is excluded from the timing."""
+    """The oracle as it is, on `layers` layer calls of the workload (C tokens
+    each); input regeneration (the synthetic bank bytes) is excluded from the
+    timing.  Each distinct selected expert is dequantised once."""
     import numpy as np
     import oracle
     import synth
     oracle.build()
     total = 0.0
+    C = wl.C
     for l in range(layers):
-        spec = wl.bank(l)
-        Wr, x = synth.layer_inputs(wl, l, pool=0, C=1)
+        spec = wl.bank(l % wl.layers)
+        Wr, x = synth.layer_inputs(wl, l % wl.layers, pool=0, C=C)
         L = oracle.router_logits(x, Wr)
         idx = oracle.topk(L, wl.k)
-        tensors = {int(e): synth.expert_tensors(spec, int(e)) for e in idx[0]}
+        tensors = {int(e): synth.expert_tensors(spec, int(e)) for e in np.unique(idx)}
         t0 = time.perf_counter()
         L = oracle.router_logits(x, Wr)
         idx = oracle.topk(L, wl.k)
-        w = oracle.route_weights(L[0, idx[0]])
-        ys = np.empty((wl.k, wl.H))
-        for s, e in enumerate(idx[0]):
+        ys = np.empty((C, wl.k, wl.H))
+        for e in np.unique(idx):
             t = tensors[int(e)]
             g = t["globals"]
             Wg = oracle.dequant(spec.fmt, t["gate_codes"], t["gate_scales"], g[0])
             Wu = oracle.dequant(spec.fmt, t["up_codes"], t["up_scales"], g[1])
             Wd = oracle.dequant(spec.fmt, t["down_codes"], t["down_scales"], g[2])
-            ys[s] = oracle.expert_ffn(Wg, Wu, Wd, x[0])
-        oracle.combine(w, ys)
+            for tok, slot in zip(*np.nonzero(idx == e)):
+                ys[tok, slot] = oracle.expert_ffn(Wg, Wu, Wd, x[tok])
+        for tok in range(C):
+            w = oracle.route_weights(L[tok, idx[tok]])
+            oracle.combine(w, ys[tok])
         total += time.perf_counter() - t0
-    us = total / layers * 1e6
+    us = total / (layers * C) * 1e6
     return {"value": us, "unit": "us/token per MoE layer", "cores": int(oracle.lib().orc_threads()),
             "kind": "oracle",
-            "sample": f"{layers} layer-token(s) of the same workload (layer 0.., pool token 0): "
-                      "router, top-k, weights, dequantisation of the 16 selected experts, their "
-                      "FFNs and the combine; bank byte regeneration not timed"}
+            "sample": f"{layers} layer call(s) of {C} token(s) of the same workload (pool draw 0): "
+                      "router, top-k, weights, dequantisation of each distinct selected expert, "
+                      "the expert FFNs and the combine; bank byte regeneration not timed"}
 
 
 def main():
@@ -174,7 +181,7 @@ def main():
         b = rf.Bank(wl.fmt, wl.E, wl.H, wl.I, device=dev)
         sd.fill_bank(b.storage.data_ptr(), b.offsets, b.stride, spec, stream.cuda_stream)
         banks.append(b)
-        Wr, x = synth.layer_inputs(wl, l, pool=0, C=POOL)
+        Wr, x = synth.layer_inputs(wl, l, pool=0, C=POOL * wl.C)
         wrs.append(torch.from_numpy(Wr).to(dev))
         xs.append(torch.from_numpy(x).to(dev))
     torch.cuda.synchronize()
@@ -185,13 +192,14 @@ def main():
     log(f"setup {time.perf_counter() - t_setup:.1f}s: {wl.layers} layers, "
         f"{resident / 1e9:.1f} GB resident bank")
 
-    ws = rf.Workspace(wl.E, wl.H, wl.I, wl.k, 1, device=dev)
-    outs = [torch.empty((1, wl.H), dtype=torch.float32, device=dev) for _ in range(wl.layers)]
+    C = wl.C
+    ws = rf.Workspace(wl.E, wl.H, wl.I, wl.k, C, device=dev)
+    outs = [torch.empty((C, wl.H), dtype=torch.float32, device=dev) for _ in range(wl.layers)]
 
     def step(i):
         j = i % POOL
         for l in range(wl.layers):
-            rf.moe_layer_fwd(banks[l], wrs[l], xs[l][j:j + 1], 1, wl.k, outs[l], ws=ws)
+            rf.moe_layer_fwd(banks[l], wrs[l], xs[l][j * C:(j + 1) * C], C, wl.k, outs[l], ws=ws)
 
     # ---- whole path ----
     for i in range(args.warmup):
@@ -207,27 +215,31 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = e0.elapsed_time(e1) / args.steps
-    us_layer = ms_step * 1000.0 / wl.layers
+    us_call = ms_step * 1000.0 / wl.layers          # one moe_layer_fwd call (C tokens)
+    us_layer = us_call / C                          # per token per MoE layer
 
-    # ---- the expert weight stream alone (dominant work), same stream ----
-    idx = [[torch.empty((1, wl.k), dtype=torch.int32, device=dev) for _ in range(POOL)]
+    # ---- the expert work alone (selection given) and the routing alone ----
+    idx = [[torch.empty((C, wl.k), dtype=torch.int32, device=dev) for _ in range(POOL)]
            for _ in range(wl.layers)]
-    wts = [[torch.empty((1, wl.k), dtype=torch.float32, device=dev) for _ in range(POOL)]
+    wts = [[torch.empty((C, wl.k), dtype=torch.float32, device=dev) for _ in range(POOL)]
            for _ in range(wl.layers)]
     for l in range(wl.layers):
         for j in range(POOL):
-            rf.moe_route(xs[l][j:j + 1], wrs[l], None, 1, wl.H, wl.E, wl.k, idx[l][j], wts[l][j], ws)
+            rf.moe_route(xs[l][j * C:(j + 1) * C], wrs[l], None, C, wl.H, wl.E, wl.k,
+                         idx[l][j], wts[l][j], ws)
     torch.cuda.synchronize()
 
     def expert_step(i):
         j = i % POOL
         for l in range(wl.layers):
-            rf.moe_expert_fwd(banks[l], xs[l][j:j + 1], 1, wl.k, idx[l][j], wts[l][j], outs[l], ws)
+            rf.moe_expert_fwd(banks[l], xs[l][j * C:(j + 1) * C], C, wl.k, idx[l][j], wts[l][j],
+                              outs[l], ws)
 
     def route_step(i):
         j = i % POOL
         for l in range(wl.layers):
-            rf.moe_route(xs[l][j:j + 1], wrs[l], None, 1, wl.H, wl.E, wl.k, idx[l][j], wts[l][j], ws)
+            rf.moe_route(xs[l][j * C:(j + 1) * C], wrs[l], None, C, wl.H, wl.E, wl.k,
+                         idx[l][j], wts[l][j], ws)
 
     def timed(fn, n):
         for i in range(max(2, args.warmup // 2)):
@@ -243,17 +255,22 @@ def main():
 
     us_expert = timed(expert_step, args.steps) if not args.layer_only else float("nan")
     us_route = timed(route_step, args.steps) if not args.layer_only else float("nan")
-    # distinct experts per call (C = 1: always k)
+    # distinct experts per call
     uniq = np.mean([len(np.unique(idx[l][j].cpu().numpy())) for l in range(wl.layers)
                     for j in range(POOL)])
     spec0 = wl.bank(0)
     sel_bytes = uniq * expert_bytes(spec0)
     router_bytes = wl.E * wl.H * 4
-    gbps_layer = sel_bytes / (us_layer * 1e-6) / 1e9
+    gbps_layer = sel_bytes / (us_call * 1e-6) / 1e9
     # the layer kernel's algorithmic bytes: router weights + selected experts
-    # (+ x in, y out: 2 * H * 4, negligible but counted)
-    alg_bytes = router_bytes + sel_bytes + 2 * wl.H * 4
-    gbps_kernel = alg_bytes / (us_layer * 1e-6) / 1e9
+    # (+ x in, y out, negligible but counted)
+    alg_bytes = router_bytes + sel_bytes + 2 * C * wl.H * 4
+    gbps_kernel = alg_bytes / (us_call * 1e-6) / 1e9
+    fmt = "nvfp4" if wl.fmt == synth.FMT_NV else "mxfp4"
+    if C == 1 and wl.name != "tiny":
+        kernel = "k_moe1 (whole layer, one launch per moe_layer_fwd call)"
+    else:
+        kernel = "k_route + k_gate_up + k_down (+ k_zero_uncovered) per moe_layer_fwd call"
 
     result = {
         "metric": METRIC,
@@ -267,26 +284,29 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
-        "data": "synthetic (seeded NVFP4 bank generated on device, fp32 N(0,1) tokens, N(0,0.02) router)",
-        "config": {"workload": f"{wl.name}: {wl.layers} MoE layers x {wl.E} experts, top-{wl.k}, "
-                               f"H {wl.H}, I {wl.I}, NVFP4, batch 1, "
+        "data": f"synthetic (seeded {fmt} bank generated on device, fp32 N(0,1) tokens, "
+                "N(0,0.02) router)",
+        "config": {"workload": f"{wl.name}: {wl.layers} MoE layer(s) x {wl.E} experts, top-{wl.k}, "
+                               f"H {wl.H}, I {wl.I}, {fmt}, {C} token(s) per call, "
                                + ("uniform (natural) routing" if wl.routing == "natural"
                                   else f"Zipf s={wl.zipf_s} routing"),
                    "layers": wl.layers, "experts": wl.E, "top_k": wl.k, "hidden": wl.H,
-                   "inter": wl.I, "format": "nvfp4", "tokens_per_call": 1},
+                   "inter": wl.I, "format": fmt, "tokens_per_call": C},
+        "us_per_call": round(us_call, 3),
         "hbm_gbps_selected_expert_bytes": round(gbps_layer, 1),
         "hbm_frac_of_peak": round(gbps_layer / HBM_PEAK_GBPS, 4),
-        "tokens_per_s": round(1000.0 / ms_step, 2),
-        "selected_expert_bytes_per_layer": int(sel_bytes),
+        "tokens_per_s": round(1000.0 * C / ms_step, 2),
+        "distinct_experts_per_call": round(float(uniq), 2),
+        "selected_expert_bytes_per_call": int(sel_bytes),
         "router_bytes_per_layer": router_bytes,
-        "us_per_layer_route": None if args.layer_only else round(us_route, 3),
-        "us_per_layer_experts": None if args.layer_only else round(us_expert, 3),
+        "us_per_call_route": None if args.layer_only else round(us_route, 3),
+        "us_per_call_experts": None if args.layer_only else round(us_expert, 3),
         "roofline": {"bound": "hbm", "achieved": round(gbps_kernel, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(gbps_kernel / HBM_PEAK_GBPS, 4),
                      "traffic": measured_traffic() if wl.name == "k3_stack" else None,
-                     "kernel": "k_moe1 (whole layer, one launch per moe_layer_fwd call)",
+                     "kernel": kernel,
                      "bytes_per_launch": int(alg_bytes),
-                     "us_per_launch": round(us_layer, 3)},
+                     "us_per_launch": round(us_call, 3)},
         "wall_s_timed": round(wall, 3),
     }
     if not args.no_cpu_baseline:

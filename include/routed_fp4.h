@@ -96,15 +96,21 @@ typedef struct {
 moe_status moe_bank_layout(int32_t format, int32_t hidden, int32_t inter,
                            int64_t offset[MOE_NUM_TENSORS], int64_t *expert_stride);
 
-/* Limits of the decode path. */
+/* Limits.  Up to MOE_MAX_DECODE_TOKENS tokens per call the router is a
+ * split-K mat-vec; more tokens (up to MOE_MAX_TOKENS, e.g. a prefill chunk)
+ * take the batched path, whose router and expert products run on the matrix
+ * cores.  The batched expert path needs H and I to be multiples of 128. */
 #define MOE_MAX_EXPERTS 1024
 #define MOE_MAX_TOPK 32
 #define MOE_MAX_DECODE_TOKENS 16
+#define MOE_MAX_TOKENS 4096
 
 /* Bytes of device workspace the calls below need for C tokens.  The workspace
- * holds router partial sums, the selection, the expert dispatch table, the
- * intermediate activations and per-slot expert outputs, and a few counters.
- * Returns 0 for arguments outside the supported range. */
+ * holds router partial sums and logits, the selection, the expert dispatch
+ * tables, the intermediate activations, one output row per (token, slot) and a
+ * few counters: about C*k*(4H + 6I) + 6*C*H bytes plus small terms (1.2 GB for
+ * C = 2048, k = 16, H = 7168, I = 1536).  Returns 0 for arguments outside the
+ * supported range (1 <= C <= MOE_MAX_TOKENS). */
 size_t moe_workspace_size(int32_t num_experts, int32_t hidden, int32_t inter,
                           int32_t top_k, int32_t C);
 
@@ -124,7 +130,9 @@ moe_status moe_workspace_init(void *ws, size_t ws_bytes, void *stream);
  *           logit descending, equal logits by ascending index (-0 == +0; NaN
  *           ranks below every number).
  *  topk_w   [C][k] fp32 out: sigmoid(logit) / sum over the k of sigmoid(logit).
- * 1 <= C <= MOE_MAX_DECODE_TOKENS, 1 <= k <= min(E, MOE_MAX_TOPK), H % 32 == 0. */
+ * 1 <= C <= MOE_MAX_TOKENS, 1 <= k <= min(E, MOE_MAX_TOPK), H % 32 == 0.
+ * For C > MOE_MAX_DECODE_TOKENS the logits come from fp32 matrix-core
+ * products (same fp32 arithmetic, another summation order). */
 moe_status moe_route(const float *x, const float *w_router, float *logits, int32_t C,
                      int32_t H, int32_t E, int32_t k, int32_t *topk_idx, float *topk_w,
                      void *ws, size_t ws_bytes, void *stream);
@@ -132,10 +140,15 @@ moe_status moe_route(const float *x, const float *w_router, float *logits, int32
 /* Selected experts and their weighted sum, for a given selection:
  *   out[t] = sum_{s<k} topk_w[t][s] * W_down,e (silu(W_gate,e x_t) * (W_up,e x_t)),
  *   e = topk_idx[t][s], summed in slot order s = 0..k-1.
- * Each distinct expert's weights are read once per call for all the tokens
- * that selected it ("MUL_MAT_ID" of the "Kimi-K3 on 2x A40" page).
+ * Each distinct expert's weights are read once per call (once per tile of up
+ * to 64 of its tokens when C > 64) for all the tokens that selected it
+ * ("MUL_MAT_ID" of the "Kimi-K3 on 2x A40" page).  One token on a shape the
+ * single-launch decode kernel is built for runs there; otherwise the batched
+ * path runs (H, I multiples of 128), or for C <= MOE_MAX_DECODE_TOKENS and
+ * other shapes the per-expert mat-vec kernels.
  *  x   [C][H] fp32 in; out [C][H] fp32 out (may not alias x).
- * Expert indices must be in [0, E) and distinct within a token. */
+ * Expert indices must be in [0, E) and distinct within a token; an index
+ * outside [0, E) is skipped (its slot contributes zero). */
 moe_status moe_expert_fwd(const moe_bank *bank, const float *x, int32_t C, int32_t k,
                           const int32_t *topk_idx, const float *topk_w, float *out,
                           void *ws, size_t ws_bytes, void *stream);

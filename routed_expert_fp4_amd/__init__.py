@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(HERE, "libroutedfp4.so")
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_DEVICE = 0, -1, -2, -3, -4
 MOE_FMT_MXFP4, MOE_FMT_NVFP4 = 1, 2
 MOE_NUM_TENSORS = 7
-MOE_MAX_EXPERTS, MOE_MAX_TOPK, MOE_MAX_DECODE_TOKENS = 1024, 32, 16
+MOE_MAX_EXPERTS, MOE_MAX_TOPK, MOE_MAX_DECODE_TOKENS, MOE_MAX_TOKENS = 1024, 32, 16, 4096
 BLOCK = {MOE_FMT_MXFP4: 32, MOE_FMT_NVFP4: 16}
 
 EXPORTS = ("moe_version", "moe_status_string", "moe_bank_layout", "moe_workspace_size",

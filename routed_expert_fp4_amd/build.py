@@ -10,7 +10,7 @@ import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SRC = os.path.join(HERE, "csrc", "routed_fp4.hip")
+SRCS = [os.path.join(HERE, "csrc", "routed_fp4.hip"), os.path.join(HERE, "csrc", "batched.hip")]
 OUT = os.path.join(HERE, "libroutedfp4.so")
 INCLUDE = os.path.join(ROOT, "include")
 
@@ -20,16 +20,17 @@ HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-shared", f"--offload-arch={ARCH}",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
-def hipcc(src: str, out: str, extra=()) -> str:
+def hipcc(srcs, out: str, extra=()) -> str:
+    srcs = [srcs] if isinstance(srcs, str) else list(srcs)
     tmp = out + ".tmp"
-    cmd = [HIPCC, *HIP_FLAGS, f"-I{INCLUDE}", *extra, src, "-o", tmp]
+    cmd = [HIPCC, *HIP_FLAGS, f"-I{INCLUDE}", *extra, *srcs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
+        raise RuntimeError(f"hipcc failed for {srcs}:\n{r.stderr}")
     os.replace(tmp, out)
     return out
 
 
 def build_library() -> str:
     """Compile the HIP kernels and the C ABI into libroutedfp4.so."""
-    return hipcc(SRC, OUT)
+    return hipcc(SRCS, OUT)

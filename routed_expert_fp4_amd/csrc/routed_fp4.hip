@@ -34,154 +34,11 @@
 #include <string.h>
 
 #include "routed_fp4.h"
+#include "common.h"
 
 namespace {
 
-constexpr int kWG = 256;           // threads per workgroup (4 waves of 64)
-constexpr int kKsplitMax = 4;      // router split-K factor limit
-constexpr int kGuRows = 16;        // gate/up: I rows per item (one per lane group)
-constexpr int kDnRowsPerGroup = 4; // down: rows per 16-lane group
-constexpr int kDnRows = 16 * kDnRowsPerGroup;  // down: H rows per item
-constexpr int kXsFloats = 10240;   // LDS floats for staged activations (40 KiB)
-constexpr int kRouteXs = 8192;     // LDS floats for the router's x tile (32 KiB)
-constexpr int kLogitCopies = 16;   // batch-1 kernel: replicas of the tagged logits
-
-// ---------------------------------------------------------------------------
-// Workspace layout
-// ---------------------------------------------------------------------------
-struct WsLayout {
-  size_t ctrl, dtick, lpart, logits, idx, w, disp, h, part, tlogits, th, tpart, total;
-};
-
-inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
-
-WsLayout ws_layout(int E, int H, int I, int k, int C) {
-  WsLayout L;
-  size_t o = 0;
-  const size_t CK = (size_t)C * k;
-  L.ctrl = o;   o = align256(o + 64 * sizeof(uint32_t));
-  L.dtick = o;  o = align256(o + (size_t)((H + kDnRows - 1) / kDnRows) * sizeof(uint32_t));
-  L.lpart = o;  o = align256(o + (size_t)kKsplitMax * C * E * sizeof(float));
-  L.logits = o; o = align256(o + (size_t)C * E * sizeof(float));
-  L.idx = o;    o = align256(o + CK * sizeof(int32_t));
-  L.w = o;      o = align256(o + CK * sizeof(float));
-  L.disp = o;   o = align256(o + (16 + 2 * CK + CK * C) * sizeof(int32_t));
-  L.h = o;      o = align256(o + CK * I * sizeof(float));
-  L.part = o;   o = align256(o + CK * H * sizeof(float));
-  // batch-1 kernel: (epoch, value) words
-  L.tlogits = o; o = align256(o + (size_t)kLogitCopies * E * sizeof(uint64_t));
-  L.th = o;      o = align256(o + (size_t)k * I * sizeof(uint64_t));
-  L.tpart = o;   o = align256(o + (size_t)k * H * sizeof(uint64_t));
-  L.total = o;
-  return L;
-}
-
-// Dispatch table (int32): [0] number of distinct experts U; then
-// uexp[CK] (expert id of distinct expert u), untok[CK] (tokens that chose it),
-// upair[CK][C] (their (token, slot) pairs p = t*k + s, in token order).
-__host__ __device__ inline int disp_uexp(int) { return 16; }
-__host__ __device__ inline int disp_untok(int CK) { return 16 + CK; }
-__host__ __device__ inline int disp_upair(int CK) { return 16 + 2 * CK; }
-
-// ---------------------------------------------------------------------------
-// Small device helpers
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ float e8m0_to_f32(uint32_t b) {
-  // 2^(b-127); b = 0 is the fp32 subnormal 2^-127; 0xFF is NaN.
-  const uint32_t u = (b == 0u) ? 0x00400000u : ((b == 255u) ? 0x7FC00000u : (b << 23));
-  return __uint_as_float(u);
-}
-
-__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
-  // OCP fp8 e4m3 ("FN": bias 7, no infinities, S.1111.111 is NaN), decoded by
-  // the hardware conversion of the low byte.
-  return __builtin_amdgcn_cvt_f32_fp8((int)(b & 0xFFu), 0);
-}
-
-// Two e2m1 elements of byte `sel` of `w`: element 2j (bits 3..0) in .x and
-// element 2j+1 (bits 7..4) in .y, unscaled (the scale operand is 1.0).
-template <int SEL>
-__device__ __forceinline__ float2 fp4x2(uint32_t w) {
-  auto v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, SEL);
-  return make_float2(v[0], v[1]);
-}
-
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-  return v;
-}
-
-__device__ __forceinline__ float group16_sum(float v) {
-#pragma unroll
-  for (int m = 8; m >= 1; m >>= 1) v += __shfl_xor(v, m, 16);
-  return v;
-}
-
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
-
-// Orderable key of an fp32 logit: larger logit -> larger key; -0 == +0;
-// NaN -> 0 (below every number).
-__device__ __forceinline__ uint32_t logit_key(float l) {
-  if (l != l) return 0u;
-  uint32_t u = __float_as_uint(l);
-  if ((u & 0x7FFFFFFFu) == 0u) u = 0u;
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-// Cross-workgroup hand-off without cache-maintenance fences.  An agent-scope
-// fence on gfx950 writes back and invalidates the XCD's L2 (about a
-// microsecond, serialised per XCD), so the kernels never use one.  Instead the
-// data one workgroup hands to another is written with agent-coherent stores
-// (sc1), each producer waits for its stores to complete before it takes a
-// ticket with a relaxed device-scope atomic, and the consumer that draws the
-// last ticket reads the data with agent-coherent loads.
-__device__ __forceinline__ void store_coherent(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// Bulk coherent reads go through buffer loads with the sc1 cache-policy bit:
-// unlike atomic loads they are not serialised one round trip at a time.
-// (Buffer resource word 3 for gfx9-family raw buffers; out-of-range offsets
-// read zero.)
-constexpr int kCachePolicySc1 = 16;
-constexpr int kCachePolicyNt = 2;   // non-temporal: weights are read once per call
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_view(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-__device__ __forceinline__ float coherent_ld(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
-  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)byte_off, 0, kCachePolicySc1));
-}
-__device__ __forceinline__ float4 coherent_ld4(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
-  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, kCachePolicySc1);
-  return make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]),
-                     __uint_as_float(v[3]));
-}
-// All of this workgroup's stores are complete, then one ticket; returns true
-// (in every thread) for the workgroup that drew ticket n-1.
-__device__ __forceinline__ bool last_to_arrive(uint32_t* ticket, uint32_t n, int* s_flag) {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (threadIdx.x == 0)
-    *s_flag = (__hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-               n - 1u) ? 1 : 0;
-  __syncthreads();
-  return *s_flag != 0;
-}
-__device__ __forceinline__ void reset_ticket(uint32_t* ticket) {
-  __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Inclusive prefix sum over the 64 lanes of a wave (lane order).
-__device__ __forceinline__ int wave_incl_scan(int v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int o = __shfl_up(v, d, 64);
-    if (lane >= d) v += o;
-  }
-  return v;
-}
+using namespace rf4;
 
 // ---------------------------------------------------------------------------
 // Router
@@ -367,13 +224,6 @@ __device__ void wave_tournament(uint32_t (&key)[N], uint32_t (&ix)[N], float (&l
     }
   }
   (void)lane;
-}
-
-// sigmoid(l_s) / sum over the k of sigmoid(l), for lane s < k of a wave
-// (the same value in every lane's sum: the butterfly adds pairs commutatively).
-__device__ __forceinline__ float route_weight(float l, int lane, int k) {
-  const float sg = (lane < k) ? 1.0f / (1.0f + expf(-l)) : 0.0f;
-  return sg / wave_sum(sg);
 }
 
 // Top-k of token t by one wave of the router's last workgroup.
@@ -921,10 +771,7 @@ struct Moe1Shared {
     float xs[kMaxH1 + kMaxH1 / 8];   // x, padded 4 floats per 32 (router, gate/up)
     float hs[kMaxI1 + kMaxI1 / 8];   // h of the slot (down)
   } u;
-  uint64_t cand_key[64];          // the selection's candidates (wave 0)
-  float cand_l[64];
-  int32_t sel_e[MOE_MAX_TOPK];     // the selection in rank order
-  float sel_l[MOE_MAX_TOPK];
+  SelectLds sel;                   // wave 0's selection scratch
   float ys[kWG1];                  // the combining slice's own rows (R <= kWG1)
   int32_t sidx[MOE_MAX_TOPK];
   float sw[MOE_MAX_TOPK];
@@ -1002,102 +849,6 @@ __device__ __forceinline__ void moe1_router_finish(const Moe1Args& a, Moe1Shared
   __syncthreads();
 }
 
-// Selection key of expert e with logit l: larger is better; equal logits go
-// to the lower index; 0 marks an empty entry (every real key is above it).
-__device__ __forceinline__ uint64_t sel_key(float l, int e) {
-  return ((uint64_t)logit_key(l) << 32) | (uint64_t)(~(uint32_t)e);
-}
-
-__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l) {
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
-  return ((uint64_t)hi << 32) | lo;
-}
-
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
-  const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, m, 64);
-  const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), m, 64);
-  return ((uint64_t)hi << 32) | lo;
-}
-
-// Orders LDS accesses of one wave (a compiler fence only: a wave's LDS
-// operations complete in issue order).
-__device__ __forceinline__ void wave_lds_fence() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-// Exact top-k of the entries one wave holds, NPL per lane (key ck[i], logit
-// lv[i]; empty entries have key 0), k <= 32 and at least k entries non-empty.
-// Writes the winners' experts and logits, best first, to S.sel_e / S.sel_l.
-//
-// A threshold first: T = the k-th largest of the 64 lane maxima.  The k lanes
-// whose maxima are >= T hold k entries >= T, so the top k are all >= T.  The
-// entries >= T (usually a few more than k) are gathered one per lane, and each
-// one's rank is the number of gathered keys above it.  When more than 64
-// entries pass the threshold (heavily clustered winners), k rounds of "take
-// the wave's best remaining entry" do the job instead.
-template <int NPL>
-__device__ void wave_select(uint64_t (&ck)[NPL], const float (&lv)[NPL], int k, Moe1Shared& S) {
-  const int lane = threadIdx.x & 63;
-  uint64_t m = 0;
-#pragma unroll
-  for (int i = 0; i < NPL; ++i) m = ck[i] > m ? ck[i] : m;
-  int r = 0;                                   // rank of this lane's maximum
-  for (int j = 0; j < 64; ++j) r += readlane_u64(m, j) > m ? 1 : 0;
-  // non-empty maxima are distinct, so exactly one lane has rank k - 1
-  const unsigned long long at = __ballot(r == k - 1);
-  const uint64_t T = at ? readlane_u64(m, __ffsll((long long)at) - 1) : 0;
-  int n = 0;
-  unsigned long long pass[NPL];
-#pragma unroll
-  for (int i = 0; i < NPL; ++i) {
-    pass[i] = __ballot(ck[i] >= T && ck[i] != 0);
-    n += __popcll(pass[i]);
-  }
-  if (n <= 64) {
-    int base = 0;
-#pragma unroll
-    for (int i = 0; i < NPL; ++i) {
-      if ((pass[i] >> lane) & 1ull) {
-        const int pos = base + __popcll(pass[i] & ((1ull << lane) - 1ull));
-        S.cand_key[pos] = ck[i];
-        S.cand_l[pos] = lv[i];
-      }
-      base += __popcll(pass[i]);
-    }
-    wave_lds_fence();
-    const uint64_t mine = lane < n ? S.cand_key[lane] : 0;
-    const float ml = lane < n ? S.cand_l[lane] : 0.0f;
-    int rk = 0;
-    for (int j = 0; j < n; ++j) rk += readlane_u64(mine, j) > mine ? 1 : 0;
-    if (lane < n && rk < k) {
-      S.sel_e[rk] = (int32_t)~(uint32_t)mine;
-      S.sel_l[rk] = ml;
-    }
-  } else {
-    for (int s = 0; s < k; ++s) {
-      uint64_t b = 0;
-#pragma unroll
-      for (int i = 0; i < NPL; ++i) b = ck[i] > b ? ck[i] : b;
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const uint64_t o = shfl_xor_u64(b, d);
-        b = o > b ? o : b;
-      }
-#pragma unroll
-      for (int i = 0; i < NPL; ++i) {
-        if (b != 0 && ck[i] == b) {          // one entry of one lane
-          S.sel_e[s] = (int32_t)~(uint32_t)b;
-          S.sel_l[s] = lv[i];
-          ck[i] = 0;
-        }
-      }
-    }
-  }
-  wave_lds_fence();
-}
-
 // The selection, computed by every workgroup for itself from the tagged
 // logits (or taken from the caller when the selection is given).  Wave 0
 // polls one replica of the logits (expert lane + 64 i in lane, slot i) and
@@ -1138,11 +889,11 @@ __device__ void moe1_routing(const Moe1Args& a, Moe1Shared& S, uint32_t epoch, b
         }
         __builtin_amdgcn_s_sleep(2);
       }
-      wave_select<NPL>(ck, lv, k, S);
-      const float l = lane < k ? S.sel_l[lane] : 0.0f;
+      wave_select<NPL>(ck, lv, k, S.sel);
+      const float l = lane < k ? S.sel.sel_l[lane] : 0.0f;
       const float w = route_weight(l, lane, k);
       if (lane < k) {
-        const int e = S.sel_e[lane];
+        const int e = S.sel.sel_e[lane];
         S.sidx[lane] = e;
         S.sw[lane] = w;
         if (writer && a.idx_out) a.idx_out[lane] = e;
@@ -1731,7 +1482,8 @@ moe_status launch_moe1(const moe_bank* b, const float* Wr, const float* x, int k
                                     : launch_moe1_fmt<MOE_FMT_NVFP4>(a, st);
 }
 
-bool tokens_ok(int C) { return C >= 1 && C <= MOE_MAX_DECODE_TOKENS; }
+bool tokens_ok(int C) { return C >= 1 && C <= MOE_MAX_TOKENS; }
+bool batched_shape(const moe_bank* b) { return b->hidden % 128 == 0 && b->inter % 128 == 0; }
 bool topk_ok(int k, int E) { return k >= 1 && k <= MOE_MAX_TOPK && k <= E; }
 
 }  // namespace
@@ -1798,9 +1550,13 @@ moe_status moe_route(const float* x, const float* w_router, float* logits, int32
     return MOE_ERR_INVALID_ARG;
   }
   if (!ws) return MOE_ERR_WORKSPACE;
-  // the router needs only the counters and partial sums: size for I = 32
+  // the router needs only the counters, partial sums and logits: size for I = 32
   const WsLayout L = ws_layout(E, H, 32, k, C);
   if (ws_bytes < L.total || !aligned(ws, 256)) return MOE_ERR_WORKSPACE;
+  if (C > MOE_MAX_DECODE_TOKENS)
+    return launch_batched_route(x, w_router, x ? nullptr : logits, x ? logits : nullptr, C, H, E,
+                                k, topk_idx, topk_w, static_cast<uint8_t*>(ws), L,
+                                reinterpret_cast<hipStream_t>(stream));
   return launch_route(x, w_router, x ? nullptr : logits, x ? logits : nullptr, C, H, E, k,
                       topk_idx, topk_w, nullptr, static_cast<uint8_t*>(ws), L,
                       reinterpret_cast<hipStream_t>(stream));
@@ -1824,6 +1580,9 @@ moe_status moe_expert_fwd(const moe_bank* bank, const float* x, int32_t C, int32
                                      w8, L, st);
     if (m != MOE_ERR_UNSUPPORTED) return m;
   }
+  if (batched_shape(bank))
+    return launch_batched_experts(bank, x, C, k, topk_idx, topk_w, out, w8, L, st);
+  if (C > MOE_MAX_DECODE_TOKENS) return MOE_ERR_UNSUPPORTED;
   hipLaunchKernelGGL(k_dispatch, dim3(1), dim3(kWG), 0, st, topk_idx,
                      reinterpret_cast<int32_t*>(w8 + L.disp), C, k, bank->num_experts);
   if ((s = launch_status()) != MOE_OK) return s;
@@ -1849,9 +1608,16 @@ moe_status moe_layer_fwd(const moe_bank* bank, const float* w_router, const floa
     const moe_status m = launch_moe1(bank, w_router, x, k, nullptr, nullptr, idx, w, out, w8, L, st);
     if (m != MOE_ERR_UNSUPPORTED) return m;
   }
-  s = launch_route(x, w_router, nullptr, nullptr, C, bank->hidden, bank->num_experts, k, idx, w,
-                   reinterpret_cast<int32_t*>(w8 + L.disp), w8, L, st);
+  const bool batched = batched_shape(bank);
+  if (!batched && C > MOE_MAX_DECODE_TOKENS) return MOE_ERR_UNSUPPORTED;
+  if (C > MOE_MAX_DECODE_TOKENS)
+    s = launch_batched_route(x, w_router, nullptr, nullptr, C, bank->hidden, bank->num_experts, k,
+                             idx, w, w8, L, st);
+  else
+    s = launch_route(x, w_router, nullptr, nullptr, C, bank->hidden, bank->num_experts, k, idx, w,
+                     batched ? nullptr : reinterpret_cast<int32_t*>(w8 + L.disp), w8, L, st);
   if (s != MOE_OK) return s;
+  if (batched) return launch_batched_experts(bank, x, C, k, idx, w, out, w8, L, st);
   return launch_experts(bank, x, C, k, idx, w, out, w8, L, st);
 }
 

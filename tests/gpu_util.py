@@ -44,10 +44,14 @@ def to_dev(a, dtype=None):
     return t.to("cuda")
 
 
-def route_depth(H: int) -> int:
-    """Upper bound on the rounding chain of the kernel's fp32 logit: each lane
-    sums H/64 or fewer products in sequence (4 per float4 load), a 6-level
-    wave reduction, and at most 4 split-K partials added in order."""
+def route_depth(H: int, C: int = 1) -> int:
+    """Upper bound on the rounding chain of the kernel's fp32 logit.  Up to 16
+    tokens: each lane sums H/64 or fewer products in sequence (4 per float4
+    load), a 6-level wave reduction, and at most 4 split-K partials added in
+    order.  More tokens: the matrix-core router accumulates the H products into
+    one fp32 accumulator; H roundings bound any order it may use."""
+    if C > 16:
+        return H + 16
     return H // 32 + 16
 
 

@@ -60,7 +60,9 @@ def test_workspace_size(rf):
     n1 = rf.moe_workspace_size(896, 7168, 1536, 16, 1)
     n7 = rf.moe_workspace_size(896, 7168, 1536, 16, 7)
     assert 0 < n1 < n7 < 64 << 20
-    assert rf.lib().moe_workspace_size(896, 7168, 1536, 16, 17) == 0     # C too large
+    assert rf.lib().moe_workspace_size(896, 7168, 1536, 16, 4097) == 0   # C too large
+    n2048 = rf.moe_workspace_size(896, 7168, 1536, 16, 2048)               # prefill chunk
+    assert 1.0e9 < n2048 < 1.4e9
     assert rf.lib().moe_workspace_size(896, 7168, 1536, 33, 1) == 0     # k too large
     assert rf.lib().moe_workspace_size(4, 256, 128, 5, 1) == 0          # k > E
     assert rf.lib().moe_workspace_size(2000, 256, 128, 5, 1) == 0       # E too large
@@ -96,7 +98,8 @@ def test_layer_fwd_rejects_bad_arguments(rf):
     assert call(_bank(rf), x=None) == rf.MOE_ERR_INVALID_ARG
     assert call(_bank(rf), wr=None) == rf.MOE_ERR_INVALID_ARG
     assert call(_bank(rf), C=0) == rf.MOE_ERR_UNSUPPORTED
-    assert call(_bank(rf), C=17) == rf.MOE_ERR_UNSUPPORTED
+    assert call(_bank(rf), C=4097) == rf.MOE_ERR_UNSUPPORTED
+    assert call(_bank(rf), C=17) == rf.MOE_ERR_WORKSPACE                    # sized for C=4
     assert call(_bank(rf), k=9) == rf.MOE_ERR_UNSUPPORTED                    # k > E
     assert call(_bank(rf), ws=None) == rf.MOE_ERR_WORKSPACE
     assert call(_bank(rf), n=ws_n - 1) == rf.MOE_ERR_WORKSPACE
