@@ -29,7 +29,7 @@ if ROOT not in sys.path:
 
 METRIC = "MoE layer decode µs/token + achieved HBM GB/s (% of peak), 896 experts top-16"
 HBM_PEAK_GBPS = 8000.0
-POOL = 16
+POOL = 16            # pre-drawn inputs per layer (2 for prefill-sized calls)
 
 
 def log(*a):
@@ -43,7 +43,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="k3_stack",
                    choices=["k3_stack", "k3_stack_zipf", "w50_k16", "w50_k8", "w50_c7_k8",
-                            "w50_c7_k16", "tiny"],
+                            "w50_c7_k16", "tiny", "k3_prefill"],
                    help="k3_stack (the headline: 12 layers, uniform routing), k3_stack_zipf "
                         "(Zipf s=1.2), or one of the single-layer decode workloads")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -106,19 +106,21 @@ def expert_bytes(spec) -> int:
     return spec.expert_bytes()
 
 
-def cpu_baseline(wl, layers: int):
-    """The oracle as it is, on `layers` layer calls of the workload (C tokens
-    each); input regeneration (the synthetic bank bytes) is excluded from the
-    timing.  Each distinct selected expert is dequantised once."""
+def cpu_baseline(wl, layers: int, max_tokens: int = 8):
+    """The oracle as it is, on `layers` layer calls of the workload with at
+    most `max_tokens` tokens each (the first tokens of the call); input
+    regeneration (the synthetic bank bytes) is excluded from the timing.  Each
+    distinct selected expert is dequantised once per call."""
     import numpy as np
     import oracle
     import synth
     oracle.build()
     total = 0.0
-    C = wl.C
+    C = min(wl.C, max_tokens)
     for l in range(layers):
         spec = wl.bank(l % wl.layers)
-        Wr, x = synth.layer_inputs(wl, l % wl.layers, pool=0, C=C)
+        Wr, x = synth.layer_inputs(wl, l % wl.layers, pool=0)
+        x = np.ascontiguousarray(x[:C])
         L = oracle.router_logits(x, Wr)
         idx = oracle.topk(L, wl.k)
         tensors = {int(e): synth.expert_tensors(spec, int(e)) for e in np.unique(idx)}
@@ -139,11 +141,13 @@ def cpu_baseline(wl, layers: int):
             oracle.combine(w, ys[tok])
         total += time.perf_counter() - t0
     us = total / (layers * C) * 1e6
+    sample = f"{layers} layer call(s) of {C} token(s) of the same workload (pool draw 0"
+    if C < wl.C:
+        sample += f", the first {C} of the call's {wl.C} tokens"
+    sample += ("): router, top-k, weights, dequantisation of each distinct selected expert, "
+               "the expert FFNs and the combine; bank byte regeneration not timed")
     return {"value": us, "unit": "us/token per MoE layer", "cores": int(oracle.lib().orc_threads()),
-            "kind": "oracle",
-            "sample": f"{layers} layer call(s) of {C} token(s) of the same workload (pool draw 0): "
-                      "router, top-k, weights, dequantisation of each distinct selected expert, "
-                      "the expert FFNs and the combine; bank byte regeneration not timed"}
+            "kind": "oracle", "sample": sample}
 
 
 def main():
@@ -169,6 +173,7 @@ def main():
         sd.build()
 
     wl = synth.WORKLOADS[args.workload]
+    pool = POOL if wl.C <= 16 else 2
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
@@ -181,7 +186,7 @@ def main():
         b = rf.Bank(wl.fmt, wl.E, wl.H, wl.I, device=dev)
         sd.fill_bank(b.storage.data_ptr(), b.offsets, b.stride, spec, stream.cuda_stream)
         banks.append(b)
-        Wr, x = synth.layer_inputs(wl, l, pool=0, C=POOL * wl.C)
+        Wr, x = synth.layer_inputs(wl, l, pool=0, C=pool * wl.C)
         wrs.append(torch.from_numpy(Wr).to(dev))
         xs.append(torch.from_numpy(x).to(dev))
     torch.cuda.synchronize()
@@ -197,7 +202,7 @@ def main():
     outs = [torch.empty((C, wl.H), dtype=torch.float32, device=dev) for _ in range(wl.layers)]
 
     def step(i):
-        j = i % POOL
+        j = i % pool
         for l in range(wl.layers):
             rf.moe_layer_fwd(banks[l], wrs[l], xs[l][j * C:(j + 1) * C], C, wl.k, outs[l], ws=ws)
 
@@ -219,24 +224,24 @@ def main():
     us_layer = us_call / C                          # per token per MoE layer
 
     # ---- the expert work alone (selection given) and the routing alone ----
-    idx = [[torch.empty((C, wl.k), dtype=torch.int32, device=dev) for _ in range(POOL)]
+    idx = [[torch.empty((C, wl.k), dtype=torch.int32, device=dev) for _ in range(pool)]
            for _ in range(wl.layers)]
-    wts = [[torch.empty((C, wl.k), dtype=torch.float32, device=dev) for _ in range(POOL)]
+    wts = [[torch.empty((C, wl.k), dtype=torch.float32, device=dev) for _ in range(pool)]
            for _ in range(wl.layers)]
     for l in range(wl.layers):
-        for j in range(POOL):
+        for j in range(pool):
             rf.moe_route(xs[l][j * C:(j + 1) * C], wrs[l], None, C, wl.H, wl.E, wl.k,
                          idx[l][j], wts[l][j], ws)
     torch.cuda.synchronize()
 
     def expert_step(i):
-        j = i % POOL
+        j = i % pool
         for l in range(wl.layers):
             rf.moe_expert_fwd(banks[l], xs[l][j * C:(j + 1) * C], C, wl.k, idx[l][j], wts[l][j],
                               outs[l], ws)
 
     def route_step(i):
-        j = i % POOL
+        j = i % pool
         for l in range(wl.layers):
             rf.moe_route(xs[l][j * C:(j + 1) * C], wrs[l], None, C, wl.H, wl.E, wl.k,
                          idx[l][j], wts[l][j], ws)
@@ -257,7 +262,7 @@ def main():
     us_route = timed(route_step, args.steps) if not args.layer_only else float("nan")
     # distinct experts per call
     uniq = np.mean([len(np.unique(idx[l][j].cpu().numpy())) for l in range(wl.layers)
-                    for j in range(POOL)])
+                    for j in range(pool)])
     spec0 = wl.bank(0)
     sel_bytes = uniq * expert_bytes(spec0)
     router_bytes = wl.E * wl.H * 4

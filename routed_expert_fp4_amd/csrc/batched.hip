@@ -10,14 +10,15 @@
 // (page "Kimi-K3 on the same pod, two engines", section "Where our build is
 // still ahead": a batched prompt pass reads each expert once per chunk).
 //
-// Exactness.  Every weight e2m1 * scale is exact in bf16 (NVFP4: at most 6
+// Precision.  Every weight e2m1 * scale is exact in bf16 (NVFP4: at most 6
 // significant bits; MXFP4: a power-of-two scale), so the weights go to the
-// matrix cores as bf16 without rounding.  Activations are fp32: each is split
-// into three bf16 pieces whose sum is the fp32 value exactly (8 + 8 + 8
-// significant bits), and each piece is multiplied separately; a piece that is
-// zero for every token of a tile (bf16-exact input) is skipped.  Products are
-// therefore exact and only the fp32 accumulation rounds.  The NVFP4 per-tensor
-// scale multiplies the accumulated sums.
+// matrix cores as bf16 without rounding.  x is fp32: each value is split into
+// three bf16 pieces whose sum is the value exactly (8 + 8 + 8 significant
+// bits) and each piece is multiplied separately; a piece that is zero for every
+// token of a tile (bf16-exact input) is skipped, so the gate/up products are
+// exact and only the fp32 accumulation rounds.  The SwiGLU output h goes to the
+// down product as two pieces (hi + lo), which carry h to within 2^-17
+// relative.  The NVFP4 per-tensor scale multiplies the accumulated sums.
 //
 // Kernels, in stream order:
 //   k_bsplit    x -> three bf16 planes + per-token flags (zeroes the counters)
@@ -25,9 +26,9 @@
 //   k_bscan     offsets and the tile list (each expert's pairs in tiles of
 //               16 or 64)
 //   k_bscatter  pairs grouped by expert
-//   k_bgu       per (tile, 64 rows of I): gate and up on MFMA, SwiGLU, h as
-//               three bf16 planes
-//   k_bdn       per (tile, 64 rows of H): down on MFMA, times the routing
+//   k_bmm<GU>   per (tile, 128 rows of I): gate and up on MFMA, SwiGLU, h as
+//               two bf16 planes
+//   k_bmm<DN>   per (tile, 256 rows of H): down on MFMA, times the routing
 //               weight, one fp32 row per pair
 //   k_bcombine  out[t] = sum of its pairs' rows in slot order (deterministic)
 // and for the router of many tokens:
@@ -42,9 +43,8 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kBK = 128;             // K elements per block: 64 code bytes of a row
-constexpr int kBRows = 64;           // weight rows per workgroup (16 per wave)
-constexpr int kXStride = kBK + 8;    // bf16 per staged activation row (272 B)
+constexpr int kRmGU = 2;             // gate/up: 16-row MFMA tiles per wave (128 rows per workgroup)
+constexpr int kRmDN = 4;             // down: 16-row MFMA tiles per wave (256 rows per workgroup)
 constexpr int kRK = 32;              // router: K elements per staged chunk
 
 struct BArgs {
@@ -57,7 +57,7 @@ struct BArgs {
   const float* x;         // [C][H]
   uint16_t* xp;           // [3][C][H] bf16 planes of x
   uint32_t* xflag;        // [C]: bit 0 plane 1 non-zero, bit 1 plane 2 non-zero
-  uint16_t* hp;           // [3][C*k][I] bf16 planes of h
+  uint16_t* hp;           // [2][C*k][I] bf16 planes of h (hi, lo)
   float* part;            // [C*k][H]
   float* out;             // [C][H]
   uint32_t* count;        // [E]
@@ -210,223 +210,272 @@ __global__ __launch_bounds__(256) void k_bscatter(BArgs a) {
 // ---------------------------------------------------------------------------
 // Grouped GEMMs
 // ---------------------------------------------------------------------------
-// Shared structure of k_bgu and k_bdn.  A workgroup owns one tile (up to NTOK
-// pairs of one expert) and 64 rows of one weight matrix (two for gate/up);
-// wave w owns rows 16w..16w+15.  The K dimension runs in blocks of 128: lane l
-// reads 16 code bytes of row (l % 16) at K offset 32 * (l / 16) of the block,
-// and MFMA step s (0..3) uses its elements 8s..8s+7.  The activations are
-// staged in LDS with the same K order, so A and B agree on which K each slot
-// of the 16x16x32 product holds.  Weight loads run one block ahead.
-template <int NR>
-struct WeightRows {
-  __amdgpu_buffer_rsrc_t codes[NR], scales[NR];
-  uint32_t coff, soff;       // this lane's offsets in block 0
-  int cstep, sstep;          // bytes per K block (codes, scales)
+// k_bmm: one grouped GEMM (gate/up with SwiGLU, or down) for one tile of up
+// to NTOK = 16 * NB pairs of one expert and 64 * RM rows of each of NMAT
+// weight matrices (wave w owns rows 16 RM w .. 16 RM w + 16 RM - 1, as RM
+// MFMA row tiles).
+//
+// K runs in stages of 256 elements: lane l of a wave reads 32 contiguous code
+// bytes of row (l % 16) of each row tile, at K offset 64 (l / 16) of the
+// stage, so a row tile's loads are 16 whole 128-byte rows segments.  MFMA
+// step t (0..7) of a stage takes elements 8t..8t+7 of the lane's 64, i.e. K
+// offset 64 (l / 16) + 8 t + j for k-slot 8 (l / 16) + j of the 16x16x32
+// product; the activations are staged in LDS in plain K order and read with
+// the same mapping, so A and B agree.  Weights are loaded two stages ahead
+// (registers), the next activation stage one ahead (registers, then LDS).
+// Activation planes: x has up to 3 (skipped when zero for the whole tile),
+// h has 2 (hi + lo: h to within 2^-17 relative).
+constexpr int kSK = 256;                 // K elements per stage
+constexpr int kSStride = kSK + 8;        // bf16 per staged row (528 B)
+
+template <int FMT, int NMAT, int RM>
+struct StageW {
+  uint4 q[NMAT][RM][2];                  // 32 code bytes per row tile and matrix
+  uint32_t sc[NMAT][RM];                 // MX: 2 e8m0 bytes; NV: 4 e4m3 bytes
 };
 
-template <int FMT, int NR>
-__device__ __forceinline__ void load_block(const WeightRows<NR>& W, int kb, uint4 (&q)[NR],
-                                           uint32_t (&sc)[NR]) {
+// Loads are unconditional: a stage past the end (valid false) reads from an
+// offset beyond the buffer, which returns zeros without touching memory, so
+// the compiler can count outstanding loads exactly (no vmcnt(0) at joins).
+constexpr uint32_t kNoLoad = 0x80000000u;
+
+template <int FMT, int NMAT, int RM>
+__device__ __forceinline__ void load_stage(const __amdgpu_buffer_rsrc_t (&codes)[NMAT],
+                                           const __amdgpu_buffer_rsrc_t (&scales)[NMAT],
+                                           const uint32_t (&coff)[RM], const uint32_t (&soff)[RM],
+                                           int kb, bool valid, StageW<FMT, NMAT, RM>& W) {
 #pragma unroll
-  for (int r = 0; r < NR; ++r) {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b128(W.codes[r], (int)(W.coff + kb * W.cstep), 0,
-                                                         kCachePolicyNt);
-    q[r] = make_uint4(v[0], v[1], v[2], v[3]);
-    if (FMT == MOE_FMT_MXFP4)
-      sc[r] = __builtin_amdgcn_raw_buffer_load_b8(W.scales[r], (int)(W.soff + kb * W.sstep), 0,
-                                                  kCachePolicyNt);
-    else
-      sc[r] = __builtin_amdgcn_raw_buffer_load_b16(W.scales[r], (int)(W.soff + kb * W.sstep), 0,
-                                                   kCachePolicyNt);
+  for (int m = 0; m < NMAT; ++m) {
+#pragma unroll
+    for (int r = 0; r < RM; ++r) {
+      const int co = valid ? (int)(coff[r] + kb * (kSK / 2)) : (int)kNoLoad;
+      const int so = valid ? (int)(soff[r] + kb * (kSK / (FMT == MOE_FMT_MXFP4 ? 32 : 16))) : (int)kNoLoad;
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(codes[m], co + 16 * c, 0, kCachePolicyNt);
+        W.q[m][r][c] = make_uint4(v[0], v[1], v[2], v[3]);
+      }
+      if (FMT == MOE_FMT_MXFP4)
+        W.sc[m][r] = __builtin_amdgcn_raw_buffer_load_b16(scales[m], so, 0, kCachePolicyNt);
+      else
+        W.sc[m][r] = __builtin_amdgcn_raw_buffer_load_b32(scales[m], so, 0, kCachePolicyNt);
+    }
   }
 }
 
-// acc[r][nb] += rows r (this wave's 16) x staged columns nb*16..nb*16+15 over
-// one K block, for planes 0..np-1 of the staged activations.
-template <int FMT, int NR, int NB, int NTOK>
-__device__ __forceinline__ void mfma_block(const uint4 (&q)[NR], const uint32_t (&sc)[NR],
-                                           const uint16_t (*xs)[NTOK][kXStride], int np,
-                                           f32x4_t (&acc)[NR][NB]) {
+template <int NTOK, int PL>
+struct StageB {
+  uint4 v[PL][NTOK / 8];                 // PL planes of NTOK rows x 256 bf16 / 256 threads
+};
+
+// Activation stage kb, planes pl0 .. pl0+PL-1 (those below np), of the tile's
+// first `rows` rows (rows past cnt read as zero) into registers.
+template <int NTOK, int PL>
+__device__ __forceinline__ void load_b(__amdgpu_buffer_rsrc_t src, uint32_t plane_bytes, int row_elems,
+                                       const int* s_row, int cnt, int pl0, int np, int kb,
+                                       StageB<NTOK, PL>& B) {
+#pragma unroll
+  for (int pl = 0; pl < PL; ++pl)
+#pragma unroll
+    for (int u = 0; u < NTOK / 8; ++u) {
+      const int q = threadIdx.x + 256 * u, c = q >> 5, ch = q & 31;
+      const bool ok = c < cnt && pl0 + pl < np;
+      const uint32_t off = ok ? (uint32_t)(pl0 + pl) * plane_bytes +
+                                    ((uint32_t)s_row[c] * row_elems + kb * kSK + ch * 8) * 2u
+                              : kNoLoad;
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(src, (int)off, 0, 0);
+      B.v[pl][u] = make_uint4(v[0], v[1], v[2], v[3]);
+    }
+}
+
+// Every row is stored (rows past the tile's pairs hold zeros): a store under a
+// branch would cost the compiler its exact count of outstanding loads.
+template <int NTOK, int PL>
+__device__ __forceinline__ void store_b(uint16_t (*xs)[NTOK][kSStride], const StageB<NTOK, PL>& B) {
+#pragma unroll
+  for (int pl = 0; pl < PL; ++pl)
+#pragma unroll
+    for (int u = 0; u < NTOK / 8; ++u) {
+      const int q = threadIdx.x + 256 * u, c = q >> 5, ch = q & 31;
+      *reinterpret_cast<uint4*>(&xs[pl][c][ch * 8]) = B.v[pl][u];
+    }
+}
+
+// One K stage: for each MFMA step the weights are dequantised once and used
+// for the nbr (<= NB) column tiles and npl (<= PL) staged planes.
+template <int FMT, int NMAT, int RM, int NB, int NTOK, int PL>
+__device__ __forceinline__ void mfma_stage(const StageW<FMT, NMAT, RM>& W,
+                                           const uint16_t (*xs)[NTOK][kSStride], int npl, int nbr,
+                                           f32x4_t (&acc)[NMAT][RM][NB]) {
   const int lane = threadIdx.x & 63, g = lane >> 4, r16 = lane & 15;
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    bf16x8_t A[NR];
+  for (int t = 0; t < 8; ++t) {
+    const int c = t >> 2, s = t & 3;
+    bf16x8_t A[NMAT][RM];
 #pragma unroll
-    for (int r = 0; r < NR; ++r) {
-      const uint32_t sb = (FMT == MOE_FMT_MXFP4) ? sc[r] : ((sc[r] >> (8 * (s >> 1))) & 0xFFu);
-      A[r] = dequant8<FMT>(scale_word(q[r], s), sb);
-    }
-    for (int pl = 0; pl < np; ++pl) {
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+      for (int r = 0; r < RM; ++r) {
+        const uint32_t sb = (FMT == MOE_FMT_MXFP4) ? ((W.sc[m][r] >> (8 * c)) & 0xFFu)
+                                                   : ((W.sc[m][r] >> (8 * (2 * c + (s >> 1)))) & 0xFFu);
+        A[m][r] = dequant8<FMT>(scale_word(W.q[m][r][c], s), sb);
+      }
+#pragma unroll
+    for (int pl = 0; pl < PL; ++pl) {
+      if (pl >= npl) break;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        const bf16x8_t B = lds_bf16x8(&xs[pl][nb * 16 + r16][32 * g + 8 * s]);
+        if (nb >= nbr) break;
+        const bf16x8_t Bv = lds_bf16x8(&xs[pl][nb * 16 + r16][64 * g + 8 * t]);
 #pragma unroll
-        for (int r = 0; r < NR; ++r)
-          acc[r][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[r], B, acc[r][nb], 0, 0, 0);
+        for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+          for (int r = 0; r < RM; ++r)
+            acc[m][r][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[m][r], Bv, acc[m][r][nb], 0, 0, 0);
       }
     }
   }
 }
 
-struct TileInfo {
-  int e, cnt, np;
-};
-
-// The tile of this workgroup: its expert, its pairs (s_pair) and the rows
-// of the staged source each column reads (s_row); zero-fills the stage.
-template <int NTOK>
-__device__ __forceinline__ bool tile_setup(const BArgs& a, bool rows_are_tokens, uint16_t* xs_flat,
-                                           int xs_words, int* s_pair, int* s_row, int* s_flags,
-                                           TileInfo& T) {
+// GU: gate and up against x (K = H), SwiGLU, h out as two bf16 planes.
+// DN: down against h (K = I), times the routing weight, one fp32 row per pair.
+// NB column tiles of 16 pairs at most (the tile's own count decides how many
+// run); PL activation planes staged per K stage (all planes at once for the
+// narrow tiles, one at a time for the wide ones).
+template <int FMT, bool GU, int RM, int NB>
+__global__ __launch_bounds__(256) void k_bmm(BArgs a) {
+  constexpr int NMAT = GU ? 2 : 1;
+  constexpr int NTOK = 16 * NB;
+  constexpr int PL = NB == 1 ? (GU ? 3 : 2) : 1;
+  __shared__ __attribute__((aligned(16))) uint16_t xs[PL][NTOK][kSStride];
+  __shared__ int s_pair[NTOK], s_row[NTOK], s_flags;
   const int tile = blockIdx.y;
-  if (tile >= (int)a.meta[0]) return false;
-  T.e = a.tiles[2 * tile];
-  const int t0 = a.tiles[2 * tile + 1];
-  T.cnt = min(NTOK, (int)a.count[T.e] - t0);
+  if (tile >= (int)a.meta[0]) return;
+  const int e = a.tiles[2 * tile], t0 = a.tiles[2 * tile + 1];
+  const int cnt = min(NTOK, (int)a.count[e] - t0);
+  const int nbr = (cnt + 15) >> 4;              // column tiles that hold pairs
   const int tid = threadIdx.x;
-  if (tid == 0) *s_flags = 0;
+  if (tid == 0) s_flags = 0;
   __syncthreads();
   if (tid < NTOK) {
-    const int p = tid < T.cnt ? a.perm[a.boff[T.e] + t0 + tid] : -1;
+    const int p = tid < cnt ? a.perm[a.boff[e] + t0 + tid] : -1;
     s_pair[tid] = p;
-    const int row = p < 0 ? -1 : (rows_are_tokens ? p / a.k : p);
+    const int row = p < 0 ? -1 : (GU ? p / a.k : p);
     s_row[tid] = row;
-    if (rows_are_tokens && row >= 0) atomicOr(s_flags, (int)a.xflag[row]);
+    if (GU && row >= 0) atomicOr(&s_flags, (int)a.xflag[row]);
   }
-  for (int i = tid; i < xs_words; i += blockDim.x) reinterpret_cast<uint32_t*>(xs_flat)[i] = 0u;
   __syncthreads();
-  const int fl = rows_are_tokens ? *s_flags : 3;
-  T.np = (fl & 2) ? 3 : ((fl & 1) ? 2 : 1);
-  return true;
-}
+  const int fl = s_flags;
+  const int np = GU ? ((fl & 2) ? 3 : ((fl & 1) ? 2 : 1)) : 2;
+  const int ngr = (np + PL - 1) / PL;           // plane groups per K stage
 
-// Stage K block kb of the tile's source rows (planes 0..np-1) into LDS.
-template <int NTOK>
-__device__ __forceinline__ void stage_block(uint16_t (*xs)[NTOK][kXStride], const uint16_t* src,
-                                            size_t plane_elems, int row_elems, const int* s_row,
-                                            int cnt, int np, int kb) {
-  for (int q = threadIdx.x; q < np * NTOK * 16; q += blockDim.x) {
-    const int pl = q / (NTOK * 16), rem = q - pl * (NTOK * 16), c = rem >> 4, ch = rem & 15;
-    if (c < cnt) {
-      const uint4 v = *reinterpret_cast<const uint4*>(src + pl * plane_elems +
-                                                      (size_t)s_row[c] * row_elems + kb * kBK + ch * 8);
-      *reinterpret_cast<uint4*>(&xs[pl][c][ch * 8]) = v;
-    }
-  }
-}
-
-template <int FMT, int NB>
-__global__ __launch_bounds__(256) void k_bgu(BArgs a) {
-  constexpr int NTOK = 16 * NB;
-  __shared__ __attribute__((aligned(16))) uint16_t xs[3][NTOK][kXStride];
-  __shared__ int s_pair[NTOK], s_row[NTOK], s_flags;
-  TileInfo T;
-  if (!tile_setup<NTOK>(a, true, &xs[0][0][0], 3 * NTOK * kXStride / 2, s_pair, s_row, &s_flags, T))
-    return;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, r16 = lane & 15;
+  const int wave = tid >> 6, lane = tid & 63, g = lane >> 4, r16 = lane & 15;
   const int H = a.H, I = a.I, B = (FMT == MOE_FMT_MXFP4) ? 32 : 16;
-  const int row = blockIdx.x * kBRows + wave * 16 + r16;
-  const uint8_t* rec = a.base + (size_t)T.e * a.stride;
-  WeightRows<2> W;
-  const uint32_t cbytes = (uint32_t)I * (H / 2), sbytes = (uint32_t)I * (H / B);
-  W.codes[0] = view(rec + a.off[MOE_T_GATE_CODES], cbytes);
-  W.codes[1] = view(rec + a.off[MOE_T_UP_CODES], cbytes);
-  W.scales[0] = view(rec + a.off[MOE_T_GATE_SCALES], sbytes);
-  W.scales[1] = view(rec + a.off[MOE_T_UP_SCALES], sbytes);
-  W.coff = (uint32_t)row * (H / 2) + g * 16;
-  W.soff = (uint32_t)row * (H / B) + g * (32 / B);
-  W.cstep = kBK / 2;
-  W.sstep = kBK / B;
-  f32x4_t acc[2][NB];
-#pragma unroll
-  for (int r = 0; r < 2; ++r)
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) acc[r][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const int nkb = H / kBK;
-  uint4 q[2], qn[2];
-  uint32_t sc[2], scn[2];
-  load_block<FMT, 2>(W, 0, qn, scn);
-  for (int kb = 0; kb < nkb; ++kb) {
-    __syncthreads();
-    stage_block<NTOK>(xs, a.xp, (size_t)a.C * H, H, s_row, T.cnt, T.np, kb);
-#pragma unroll
-    for (int r = 0; r < 2; ++r) { q[r] = qn[r]; sc[r] = scn[r]; }
-    if (kb + 1 < nkb) load_block<FMT, 2>(W, kb + 1, qn, scn);
-    __syncthreads();
-    mfma_block<FMT, 2, NB, NTOK>(q, sc, xs, T.np, acc);
+  const int K = GU ? H : I, N = GU ? I : H;
+  const int row0 = blockIdx.x * (64 * RM) + wave * (16 * RM);
+  const uint8_t* rec = a.base + (size_t)e * a.stride;
+  __amdgpu_buffer_rsrc_t codes[NMAT], scales[NMAT];
+  const uint32_t cbytes = (uint32_t)N * (K / 2), sbytes = (uint32_t)N * (K / B);
+  if (GU) {
+    codes[0] = view(rec + a.off[MOE_T_GATE_CODES], cbytes);
+    scales[0] = view(rec + a.off[MOE_T_GATE_SCALES], sbytes);
+    codes[NMAT - 1] = view(rec + a.off[MOE_T_UP_CODES], cbytes);
+    scales[NMAT - 1] = view(rec + a.off[MOE_T_UP_SCALES], sbytes);
+  } else {
+    codes[0] = view(rec + a.off[MOE_T_DOWN_CODES], cbytes);
+    scales[0] = view(rec + a.off[MOE_T_DOWN_SCALES], sbytes);
   }
-  float gg = 1.0f, gu = 1.0f;
-  if (FMT == MOE_FMT_NVFP4) {
-    const float* gl = reinterpret_cast<const float*>(rec + a.off[MOE_T_GLOBALS]);
-    gg = gl[0];
-    gu = gl[1];
+  uint32_t coff[RM], soff[RM];
+#pragma unroll
+  for (int r = 0; r < RM; ++r) {
+    const int row = row0 + 16 * r + r16;
+    coff[r] = (uint32_t)row * (K / 2) + g * 32;
+    soff[r] = (uint32_t)row * (K / B) + g * (64 / B);
   }
   const size_t CK = (size_t)a.C * a.k;
-  const int irow = blockIdx.x * kBRows + wave * 16 + 4 * g;     // this lane's 4 output rows
+  const uint32_t plane_bytes = (uint32_t)((GU ? (size_t)a.C * H : CK * I) * 2);
+  const __amdgpu_buffer_rsrc_t src = view(reinterpret_cast<const uint8_t*>(GU ? a.xp : a.hp),
+                                          plane_bytes * (uint32_t)(GU ? 3 : 2));
+
+  f32x4_t acc[NMAT][RM][NB];
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const int p = s_pair[nb * 16 + r16];
-    if (p < 0) continue;
-    uint16_t hb[3][4];
+  for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float h = silu(gg * acc[0][nb][j]) * (gu * acc[1][nb][j]);
-      split3(h, hb[0][j], hb[1][j], hb[2][j]);
+    for (int r = 0; r < RM; ++r)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) acc[m][r][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // K stages in pairs (nkb is even): buffers W0/B0 serve even stages, W1/B1
+  // odd ones, so a buffer is reloaded in place after use and no register copy
+  // of an in-flight load is ever needed (a copy would wait for the load).
+  // Plane groups beyond the first (wide tiles of non-bf16-exact x only)
+  // stream the weights again.
+  const int nkb = K / kSK;
+  for (int gr = 0; gr < ngr; ++gr) {
+    const int pl0 = gr * PL, npl = min(PL, np - pl0);
+    StageW<FMT, NMAT, RM> W0, W1;
+    StageB<NTOK, PL> B0, B1;
+    load_stage<FMT, NMAT, RM>(codes, scales, coff, soff, 0, true, W0);
+    load_b<NTOK, PL>(src, plane_bytes, K, s_row, cnt, pl0, np, 0, B0);
+    load_stage<FMT, NMAT, RM>(codes, scales, coff, soff, 1, true, W1);
+    for (int kb = 0; kb < nkb; kb += 2) {
+      __syncthreads();                         // the previous stage's LDS reads are done
+      store_b<NTOK, PL>(xs, B0);
+      load_b<NTOK, PL>(src, plane_bytes, K, s_row, cnt, pl0, np, kb + 1, B1);
+      __syncthreads();
+      mfma_stage<FMT, NMAT, RM, NB, NTOK, PL>(W0, xs, npl, nbr, acc);
+      load_stage<FMT, NMAT, RM>(codes, scales, coff, soff, kb + 2, kb + 2 < nkb, W0);
+      __syncthreads();
+      store_b<NTOK, PL>(xs, B1);
+      load_b<NTOK, PL>(src, plane_bytes, K, s_row, kb + 2 < nkb ? cnt : 0, pl0, np, kb + 2, B0);
+      __syncthreads();
+      mfma_stage<FMT, NMAT, RM, NB, NTOK, PL>(W1, xs, npl, nbr, acc);
+      load_stage<FMT, NMAT, RM>(codes, scales, coff, soff, kb + 3, kb + 3 < nkb, W1);
+    }
+  }
+
+  const int orow0 = row0 + 4 * g;              // + 16 r + j: this lane's output rows
+  if (GU) {
+    float gg = 1.0f, gu = 1.0f;
+    if (FMT == MOE_FMT_NVFP4) {
+      const float* gl = reinterpret_cast<const float*>(rec + a.off[MOE_T_GLOBALS]);
+      gg = gl[0];
+      gu = gl[1];
     }
 #pragma unroll
-    for (int pl = 0; pl < 3; ++pl)
-      *reinterpret_cast<uint2*>(a.hp + (pl * CK + p) * I + irow) =
-          make_uint2((uint32_t)hb[pl][0] | ((uint32_t)hb[pl][1] << 16),
-                     (uint32_t)hb[pl][2] | ((uint32_t)hb[pl][3] << 16));
-  }
-}
-
-template <int FMT, int NB>
-__global__ __launch_bounds__(256) void k_bdn(BArgs a) {
-  constexpr int NTOK = 16 * NB;
-  __shared__ __attribute__((aligned(16))) uint16_t xs[3][NTOK][kXStride];
-  __shared__ int s_pair[NTOK], s_row[NTOK], s_flags;
-  TileInfo T;
-  if (!tile_setup<NTOK>(a, false, &xs[0][0][0], 3 * NTOK * kXStride / 2, s_pair, s_row, &s_flags, T))
-    return;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, r16 = lane & 15;
-  const int H = a.H, I = a.I, B = (FMT == MOE_FMT_MXFP4) ? 32 : 16;
-  const int row = blockIdx.x * kBRows + wave * 16 + r16;
-  const uint8_t* rec = a.base + (size_t)T.e * a.stride;
-  WeightRows<1> W;
-  W.codes[0] = view(rec + a.off[MOE_T_DOWN_CODES], (uint32_t)H * (I / 2));
-  W.scales[0] = view(rec + a.off[MOE_T_DOWN_SCALES], (uint32_t)H * (I / B));
-  W.coff = (uint32_t)row * (I / 2) + g * 16;
-  W.soff = (uint32_t)row * (I / B) + g * (32 / B);
-  W.cstep = kBK / 2;
-  W.sstep = kBK / B;
-  f32x4_t acc[1][NB];
+    for (int nb = 0; nb < NB; ++nb) {
+      const int p = s_pair[nb * 16 + r16];
+      if (p < 0) continue;
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) acc[0][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const int nkb = I / kBK;
-  const size_t CK = (size_t)a.C * a.k;
-  uint4 q[1], qn[1];
-  uint32_t sc[1], scn[1];
-  load_block<FMT, 1>(W, 0, qn, scn);
-  for (int kb = 0; kb < nkb; ++kb) {
-    __syncthreads();
-    stage_block<NTOK>(xs, a.hp, CK * I, I, s_row, T.cnt, T.np, kb);
-    q[0] = qn[0];
-    sc[0] = scn[0];
-    if (kb + 1 < nkb) load_block<FMT, 1>(W, kb + 1, qn, scn);
-    __syncthreads();
-    mfma_block<FMT, 1, NB, NTOK>(q, sc, xs, T.np, acc);
-  }
-  float gd = 1.0f;
-  if (FMT == MOE_FMT_NVFP4) gd = reinterpret_cast<const float*>(rec + a.off[MOE_T_GLOBALS])[2];
-  const int hrow = blockIdx.x * kBRows + wave * 16 + 4 * g;
+      for (int r = 0; r < RM; ++r) {
+        uint16_t hi[4], lo[4];
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const int p = s_pair[nb * 16 + r16];
-    if (p < 0) continue;
-    const float wp = a.w[p] * gd;
-    *reinterpret_cast<float4*>(a.part + (size_t)p * H + hrow) =
-        make_float4(wp * acc[0][nb][0], wp * acc[0][nb][1], wp * acc[0][nb][2], wp * acc[0][nb][3]);
+        for (int j = 0; j < 4; ++j) {
+          const float h = silu(gg * acc[0][r][nb][j]) * (gu * acc[NMAT - 1][r][nb][j]);
+          hi[j] = bf16_bits(h);
+          lo[j] = bf16_bits(h - bf16_float(hi[j]));
+        }
+        const size_t o = (size_t)p * I + orow0 + 16 * r;
+        *reinterpret_cast<uint2*>(a.hp + o) =
+            make_uint2((uint32_t)hi[0] | ((uint32_t)hi[1] << 16), (uint32_t)hi[2] | ((uint32_t)hi[3] << 16));
+        *reinterpret_cast<uint2*>(a.hp + CK * I + o) =
+            make_uint2((uint32_t)lo[0] | ((uint32_t)lo[1] << 16), (uint32_t)lo[2] | ((uint32_t)lo[3] << 16));
+      }
+    }
+  } else {
+    float gd = 1.0f;
+    if (FMT == MOE_FMT_NVFP4) gd = reinterpret_cast<const float*>(rec + a.off[MOE_T_GLOBALS])[2];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int p = s_pair[nb * 16 + r16];
+      if (p < 0) continue;
+      const float wp = a.w[p] * gd;
+#pragma unroll
+      for (int r = 0; r < RM; ++r)
+        *reinterpret_cast<float4*>(a.part + (size_t)p * H + orow0 + 16 * r) =
+            make_float4(wp * acc[0][r][nb][0], wp * acc[0][r][nb][1], wp * acc[0][r][nb][2],
+                        wp * acc[0][r][nb][3]);
+    }
   }
 }
 
@@ -520,6 +569,248 @@ __global__ __launch_bounds__(512) void k_btopk(const float* logits, int C, int E
   }
 }
 
+// ---------------------------------------------------------------------------
+// Narrow tiles (up to 16 pairs, decode batches).  Each wave streams its rows'
+// weights into registers, one K stage ahead, like the wide kernel; the
+// activations, shared by the four waves, go straight from L2 into LDS with
+// buffer_load ... lds (double-buffered, one stage ahead).  Those loads are
+// issued from inline assembly: the compiler then does not know they write
+// LDS and does not make every LDS read wait for all loads in flight; the
+// kernel waits for them explicitly, by count.
+// ---------------------------------------------------------------------------
+
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor words (the layout __builtin_amdgcn_make_buffer_rsrc
+// builds): base, stride 0, num_records, flags.
+__device__ __forceinline__ i32x4_t desc(const void* base, uint32_t bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  return i32x4_t{(int)(uint32_t)b, (int)((uint32_t)(b >> 32) & 0xFFFFu), (int)bytes, 0x00020000};
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
+}
+// lane l's 16 bytes at LDS m0 + 16 l (m0 must be the same in the whole wave)
+__device__ __forceinline__ void dma16(i32x4_t r, uint32_t m0, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds"
+               :
+               : "s"(m0), "v"(voff), "s"(r)
+               : "memory", "m0");
+}
+// lane l's 4 bytes at LDS m0 + 4 l
+__device__ __forceinline__ void dma4(i32x4_t r, uint32_t m0, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen nt lds"
+               :
+               : "s"(m0), "v"(voff), "s"(r)
+               : "memory", "m0");
+}
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+template <int FMT, bool GU, int RM>
+__global__ __launch_bounds__(256) void k_bdma(BArgs a) {
+  constexpr int NMAT = GU ? 2 : 1;
+  constexpr int NT = NMAT * RM;                       // row tiles per wave
+  constexpr int PL = GU ? 3 : 2;                      // activation planes
+  constexpr int BPLANE = 16 * 512;                    // 16 rows x 256 bf16
+  constexpr int NB_LD = PL * 2;                       // activation loads per thread per stage
+  constexpr int NW_LD = NT * 3;                       // weight loads per thread per stage
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  uint8_t* bl = smem;                                 // [2][PL][BPLANE]
+  __shared__ int s_pair[16], s_row[16], s_flags;
+
+  const int tile = blockIdx.y;
+  if (tile >= (int)a.meta[0]) return;
+  const int e = a.tiles[2 * tile], t0 = a.tiles[2 * tile + 1];
+  const int cnt = min(16, (int)a.count[e] - t0);
+  const int tid = threadIdx.x;
+  if (tid == 0) s_flags = 0;
+  __syncthreads();
+  if (tid < 16) {
+    const int p = tid < cnt ? a.perm[a.boff[e] + t0 + tid] : -1;
+    s_pair[tid] = p;
+    const int row = p < 0 ? -1 : (GU ? p / a.k : p);
+    s_row[tid] = row;
+    if (GU && row >= 0) atomicOr(&s_flags, (int)a.xflag[row]);
+  }
+  __syncthreads();
+  const int fl = s_flags;
+  const int np = GU ? ((fl & 2) ? 3 : ((fl & 1) ? 2 : 1)) : 2;
+
+  const int wave = tid >> 6, lane = tid & 63, g = lane >> 4, r16 = lane & 15;
+  const int H = a.H, I = a.I, B = (FMT == MOE_FMT_MXFP4) ? 32 : 16;
+  const int K = GU ? H : I, N = GU ? I : H;
+  const int row0 = blockIdx.x * (64 * RM) + wave * (16 * RM);
+  const uint8_t* rec = a.base + (size_t)e * a.stride;
+  __amdgpu_buffer_rsrc_t codes[NMAT], scales[NMAT];
+  const uint32_t cbytes = (uint32_t)N * (K / 2), sbytes = (uint32_t)N * (K / B);
+  codes[0] = view(rec + a.off[GU ? MOE_T_GATE_CODES : MOE_T_DOWN_CODES], cbytes);
+  scales[0] = view(rec + a.off[GU ? MOE_T_GATE_SCALES : MOE_T_DOWN_SCALES], sbytes);
+  if (GU) {
+    codes[NMAT - 1] = view(rec + a.off[MOE_T_UP_CODES], cbytes);
+    scales[NMAT - 1] = view(rec + a.off[MOE_T_UP_SCALES], sbytes);
+  }
+  uint32_t coff[RM], soff[RM];
+#pragma unroll
+  for (int r = 0; r < RM; ++r) {
+    const int row = row0 + 16 * r + r16;
+    coff[r] = (uint32_t)row * (K / 2) + g * 32;
+    soff[r] = (uint32_t)row * (K / B) + g * (64 / B);
+  }
+  const size_t CK = (size_t)a.C * a.k;
+  const uint32_t plane_bytes = (uint32_t)((GU ? (size_t)a.C * H : CK * I) * 2);
+  const i32x4_t src = desc(GU ? (const void*)a.xp : (const void*)a.hp, plane_bytes * (uint32_t)PL);
+  const uint32_t bbase = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_addr(bl));
+
+  // this thread's part of an activation stage: for plane pl, DMA slot u of
+  // wave w covers LDS bytes [(2w + u) * 1 KB, +1 KB) of the 8 KB plane, so
+  // lane l writes row P / 512, 16-byte slot (P / 16) % 32 (P = its byte); it
+  // loads the chunk that lands there under the swizzle chunk ^ (row & 15).
+  uint32_t boff[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int P = (2 * wave + u) * 1024 + lane * 16;
+    const int row = P >> 9, ch = ((P >> 4) & 31) ^ (row & 15);
+    boff[u] = (row < cnt) ? ((uint32_t)s_row[row] * (uint32_t)K + (uint32_t)ch * 8u) * 2u : kNoLoad;
+  }
+  const int nkb = K / kSK;
+  auto issue_b = [&](int kb) {
+    const uint32_t buf = bbase + (uint32_t)((kb & 1) * PL * BPLANE);
+    const bool ok = kb < nkb;
+#pragma unroll
+    for (int pl = 0; pl < PL; ++pl)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const uint32_t o = (ok && pl < np && boff[u] != kNoLoad)
+                               ? boff[u] + (uint32_t)pl * plane_bytes + (uint32_t)kb * (kSK * 2)
+                               : kNoLoad;
+        dma16(src, (uint32_t)__builtin_amdgcn_readfirstlane(
+                       (int)(buf + pl * BPLANE + (2 * wave + u) * 1024)), o);
+      }
+  };
+
+  f32x4_t acc[NMAT][RM][1];
+#pragma unroll
+  for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+    for (int r = 0; r < RM; ++r) acc[m][r][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // one K stage: activations of stage kb resident in LDS buffer kb & 1
+  auto stage = [&](int kb, const StageW<FMT, NMAT, RM>& W) {
+    const uint8_t* bb = bl + (kb & 1) * PL * BPLANE;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int c = t >> 2, s4 = t & 3;
+      bf16x8_t A[NMAT][RM];
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+        for (int r = 0; r < RM; ++r) {
+          const uint32_t sb = (FMT == MOE_FMT_MXFP4) ? ((W.sc[m][r] >> (8 * c)) & 0xFFu)
+                                                     : ((W.sc[m][r] >> (8 * (2 * c + (s4 >> 1)))) & 0xFFu);
+          A[m][r] = dequant8<FMT>(scale_word(W.q[m][r][c], s4), sb);
+        }
+      const int k16 = 8 * g + t;
+      const uint8_t* bp = bb + r16 * 512 + ((k16 ^ r16) * 16);
+#pragma unroll
+      for (int pl = 0; pl < PL; ++pl) {
+        if (pl >= np) break;
+        const bf16x8_t Bv = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(bp + pl * BPLANE));
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+          for (int r = 0; r < RM; ++r)
+            acc[m][r][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[m][r], Bv, acc[m][r][0], 0, 0, 0);
+      }
+    }
+  };
+
+  // Issue order W(0) B(0) W(1), then per stage kb: B(kb+1), [compute kb],
+  // W(kb+2).  At stage kb the loads issued after B(kb) are W(kb+1) and
+  // B(kb+1): waiting for at most NW_LD + NB_LD outstanding lands B(kb).  The
+  // weights are registers the compiler waits for itself; W0/W1 alternate so a
+  // buffer is reloaded in place after its stage (nkb is even).
+  StageW<FMT, NMAT, RM> W0, W1;
+  load_stage<FMT, NMAT, RM>(codes, scales, coff, soff, 0, true, W0);
+  issue_b(0);
+  load_stage<FMT, NMAT, RM>(codes, scales, coff, soff, 1, true, W1);
+  for (int kb = 0; kb < nkb; kb += 2) {
+    __syncthreads();                     // stage kb-1 is done: its buffer may be refilled
+    issue_b(kb + 1);
+    wait_vm<NW_LD + NB_LD>();            // this wave's activations of stage kb have landed
+    __syncthreads();                     // ... and every wave's
+    stage(kb, W0);
+    load_stage<FMT, NMAT, RM>(codes, scales, coff, soff, kb + 2, kb + 2 < nkb, W0);
+    __syncthreads();
+    issue_b(kb + 2);
+    wait_vm<NW_LD + NB_LD>();
+    __syncthreads();
+    stage(kb + 1, W1);
+    load_stage<FMT, NMAT, RM>(codes, scales, coff, soff, kb + 3, kb + 3 < nkb, W1);
+  }
+  wait_vm<0>();                          // no load may still be writing LDS at exit
+
+  const int orow0 = row0 + 4 * g;
+  const int p = s_pair[r16];
+  if (p < 0) return;
+  if (GU) {
+    float gg = 1.0f, gu = 1.0f;
+    if (FMT == MOE_FMT_NVFP4) {
+      const float* gl = reinterpret_cast<const float*>(rec + a.off[MOE_T_GLOBALS]);
+      gg = gl[0];
+      gu = gl[1];
+    }
+#pragma unroll
+    for (int r = 0; r < RM; ++r) {
+      uint16_t hi[4], lo[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float h = silu(gg * acc[0][r][0][j]) * (gu * acc[NMAT - 1][r][0][j]);
+        hi[j] = bf16_bits(h);
+        lo[j] = bf16_bits(h - bf16_float(hi[j]));
+      }
+      const size_t o = (size_t)p * I + orow0 + 16 * r;
+      *reinterpret_cast<uint2*>(a.hp + o) =
+          make_uint2((uint32_t)hi[0] | ((uint32_t)hi[1] << 16), (uint32_t)hi[2] | ((uint32_t)hi[3] << 16));
+      *reinterpret_cast<uint2*>(a.hp + CK * I + o) =
+          make_uint2((uint32_t)lo[0] | ((uint32_t)lo[1] << 16), (uint32_t)lo[2] | ((uint32_t)lo[3] << 16));
+    }
+  } else {
+    float gd = 1.0f;
+    if (FMT == MOE_FMT_NVFP4) gd = reinterpret_cast<const float*>(rec + a.off[MOE_T_GLOBALS])[2];
+    const float wp = a.w[p] * gd;
+#pragma unroll
+    for (int r = 0; r < RM; ++r)
+      *reinterpret_cast<float4*>(a.part + (size_t)p * H + orow0 + 16 * r) =
+          make_float4(wp * acc[0][r][0][0], wp * acc[0][r][0][1], wp * acc[0][r][0][2],
+                      wp * acc[0][r][0][3]);
+  }
+}
+
+template <int FMT, bool GU, int RM>
+constexpr int bdma_lds_bytes() {
+  return 2 * (GU ? 3 : 2) * 16 * 512;
+}
+
+template <int FMT, bool GU, int RM>
+moe_status launch_bdma(const BArgs& a, dim3 grid, hipStream_t st) {
+  constexpr int bytes = bdma_lds_bytes<FMT, GU, RM>();
+  static bool attr_set[64] = {false};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (!attr_set[dev]) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(k_bdma<FMT, GU, RM>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, bytes) != hipSuccess)
+      return MOE_ERR_DEVICE;
+    attr_set[dev] = true;
+  }
+  hipLaunchKernelGGL((k_bdma<FMT, GU, RM>), grid, dim3(256), bytes, st, a);
+  return MOE_OK;
+}
+
 moe_status status_of_launch() { return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_DEVICE; }
 
 }  // namespace
@@ -543,7 +834,7 @@ moe_status launch_batched_experts(const moe_bank* b, const float* x, int C, int 
                                   const int32_t* idx, const float* w, float* out, uint8_t* ws,
                                   const WsLayout& L, hipStream_t st) {
   const int H = b->hidden, I = b->inter;
-  if (H % kBK || I % kBK) return MOE_ERR_UNSUPPORTED;
+  if (!batched_shape_ok(b)) return MOE_ERR_UNSUPPORTED;
   BArgs a;
   a.base = static_cast<const uint8_t*>(b->base);
   a.stride = b->expert_stride;
@@ -568,24 +859,21 @@ moe_status launch_batched_experts(const moe_bank* b, const float* x, int C, int 
   hipLaunchKernelGGL(k_bcount, dim3((CK + 255) / 256), dim3(256), 0, st, a);
   hipLaunchKernelGGL(k_bscan, dim3(1), dim3(1024), 0, st, a);
   hipLaunchKernelGGL(k_bscatter, dim3((CK + 255) / 256), dim3(256), 0, st, a);
-  const dim3 ggu(I / kBRows, maxt), gdn(H / kBRows, maxt);
-  if (b->format == MOE_FMT_MXFP4) {
-    if (a.ntok == 16) {
-      hipLaunchKernelGGL((k_bgu<MOE_FMT_MXFP4, 1>), ggu, dim3(256), 0, st, a);
-      hipLaunchKernelGGL((k_bdn<MOE_FMT_MXFP4, 1>), gdn, dim3(256), 0, st, a);
-    } else {
-      hipLaunchKernelGGL((k_bgu<MOE_FMT_MXFP4, 4>), ggu, dim3(256), 0, st, a);
-      hipLaunchKernelGGL((k_bdn<MOE_FMT_MXFP4, 4>), gdn, dim3(256), 0, st, a);
-    }
-  } else {
-    if (a.ntok == 16) {
-      hipLaunchKernelGGL((k_bgu<MOE_FMT_NVFP4, 1>), ggu, dim3(256), 0, st, a);
-      hipLaunchKernelGGL((k_bdn<MOE_FMT_NVFP4, 1>), gdn, dim3(256), 0, st, a);
-    } else {
-      hipLaunchKernelGGL((k_bgu<MOE_FMT_NVFP4, 4>), ggu, dim3(256), 0, st, a);
-      hipLaunchKernelGGL((k_bdn<MOE_FMT_NVFP4, 4>), gdn, dim3(256), 0, st, a);
-    }
-  }
+  const dim3 ggu(I / (64 * kRmGU), maxt), gdn(H / (64 * kRmDN), maxt);
+#define RF4_BMM(F)                                                                        \
+  do {                                                                                    \
+    if (a.ntok == 16) {                                                                   \
+      moe_status m = launch_bdma<F, true, kRmGU>(a, ggu, st);                             \
+      if (m == MOE_OK) m = launch_bdma<F, false, kRmDN>(a, gdn, st);                      \
+      if (m != MOE_OK) return m;                                                          \
+    } else {                                                                              \
+      hipLaunchKernelGGL((k_bmm<F, true, kRmGU, 4>), ggu, dim3(256), 0, st, a);           \
+      hipLaunchKernelGGL((k_bmm<F, false, kRmDN, 4>), gdn, dim3(256), 0, st, a);          \
+    }                                                                                     \
+  } while (0)
+  if (b->format == MOE_FMT_MXFP4) RF4_BMM(MOE_FMT_MXFP4);
+  else RF4_BMM(MOE_FMT_NVFP4);
+#undef RF4_BMM
   hipLaunchKernelGGL(k_bcombine, dim3((H / 4 + 255) / 256, C), dim3(256), 0, st, a);
   return status_of_launch();
 }

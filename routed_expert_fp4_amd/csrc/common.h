@@ -26,7 +26,7 @@ constexpr int kLogitCopies = 16;   // batch-1 kernel: replicas of the tagged log
 struct WsLayout {
   size_t ctrl, dtick, lpart, logits, idx, w, disp, h, part, tlogits, th, tpart;
   // batched path: per-expert counts, cursors and offsets, the tile list, the
-  // (token, slot) pairs grouped by expert, x and h as three bf16 planes each
+  // (token, slot) pairs grouped by expert, x as three bf16 planes, h as two
   size_t bcount, bcursor, boff, bmeta, btile, perm, xp, xflag, hp;
   size_t total;
 };
@@ -70,7 +70,7 @@ inline WsLayout ws_layout(int E, int H, int I, int k, int C) {
   L.perm = o;    o = align256(o + CK * sizeof(int32_t));
   L.xp = o;      o = align256(o + 3 * (size_t)C * H * sizeof(uint16_t));
   L.xflag = o;   o = align256(o + (size_t)C * sizeof(uint32_t));
-  L.hp = o;      o = align256(o + 3 * CK * I * sizeof(uint16_t));
+  L.hp = o;      o = align256(o + 2 * CK * I * sizeof(uint16_t));
   L.total = o;
   return L;
 }
@@ -291,6 +291,16 @@ __device__ void wave_select(uint64_t (&ck)[NPL], const float (&lv)[NPL], int k, 
 __device__ __forceinline__ float route_weight(float l, int lane, int k) {
   const float sg = (lane < k) ? 1.0f / (1.0f + expf(-l)) : 0.0f;
   return sg / wave_sum(sg);
+}
+
+// Shapes the batched path is built for: K stages of 256 elements taken in
+// pairs, row tiles of 128 (gate/up) and 256 (down) rows, scale tensors at
+// 4-byte aligned offsets (their words are loaded whole).
+inline bool batched_shape_ok(const moe_bank* b) {
+  if (b->hidden % 512 || b->inter % 512) return false;
+  for (int t = MOE_T_GATE_SCALES; t <= MOE_T_DOWN_SCALES; ++t)
+    if (b->offset[t] % 4) return false;
+  return true;
 }
 
 // Host side of the batched path (batched.hip).  Both enqueue on `st` only.

@@ -1483,7 +1483,7 @@ moe_status launch_moe1(const moe_bank* b, const float* Wr, const float* x, int k
 }
 
 bool tokens_ok(int C) { return C >= 1 && C <= MOE_MAX_TOKENS; }
-bool batched_shape(const moe_bank* b) { return b->hidden % 128 == 0 && b->inter % 128 == 0; }
+bool batched_shape(const moe_bank* b) { return batched_shape_ok(b); }
 bool topk_ok(int k, int E) { return k >= 1 && k <= MOE_MAX_TOPK && k <= E; }
 
 }  // namespace
