@@ -45,6 +45,8 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kRmGU = 2;             // gate/up: 16-row MFMA tiles per wave (128 rows per workgroup)
 constexpr int kRmDN = 4;             // down: 16-row MFMA tiles per wave (256 rows per workgroup)
+constexpr int kRmGUn = 2;            // narrow tiles: gate/up 128 rows per workgroup
+constexpr int kRmDNn = 4;            // narrow tiles: down 256 rows per workgroup
 constexpr int kRK = 32;              // router: K elements per staged chunk
 
 struct BArgs {
@@ -340,13 +342,13 @@ __device__ __forceinline__ void mfma_stage(const StageW<FMT, NMAT, RM>& W,
 // GU: gate and up against x (K = H), SwiGLU, h out as two bf16 planes.
 // DN: down against h (K = I), times the routing weight, one fp32 row per pair.
 // NB column tiles of 16 pairs at most (the tile's own count decides how many
-// run); PL activation planes staged per K stage (all planes at once for the
-// narrow tiles, one at a time for the wide ones).
+// run); PL activation planes staged per K stage (both h planes at once; x
+// planes one group at a time for wide tiles, whose x is usually bf16-exact).
 template <int FMT, bool GU, int RM, int NB>
 __global__ __launch_bounds__(256) void k_bmm(BArgs a) {
   constexpr int NMAT = GU ? 2 : 1;
   constexpr int NTOK = 16 * NB;
-  constexpr int PL = NB == 1 ? (GU ? 3 : 2) : 1;
+  constexpr int PL = GU ? (NB == 1 ? 3 : 1) : 2;   // h: both planes at once
   __shared__ __attribute__((aligned(16))) uint16_t xs[PL][NTOK][kSStride];
   __shared__ int s_pair[NTOK], s_row[NTOK], s_flags;
   const int tile = blockIdx.y;
@@ -860,11 +862,12 @@ moe_status launch_batched_experts(const moe_bank* b, const float* x, int C, int 
   hipLaunchKernelGGL(k_bscan, dim3(1), dim3(1024), 0, st, a);
   hipLaunchKernelGGL(k_bscatter, dim3((CK + 255) / 256), dim3(256), 0, st, a);
   const dim3 ggu(I / (64 * kRmGU), maxt), gdn(H / (64 * kRmDN), maxt);
+  const dim3 ggun(I / (64 * kRmGUn), maxt), gdnn(H / (64 * kRmDNn), maxt);
 #define RF4_BMM(F)                                                                        \
   do {                                                                                    \
     if (a.ntok == 16) {                                                                   \
-      moe_status m = launch_bdma<F, true, kRmGU>(a, ggu, st);                             \
-      if (m == MOE_OK) m = launch_bdma<F, false, kRmDN>(a, gdn, st);                      \
+      moe_status m = launch_bdma<F, true, kRmGUn>(a, ggun, st);                           \
+      if (m == MOE_OK) m = launch_bdma<F, false, kRmDNn>(a, gdnn, st);                    \
       if (m != MOE_OK) return m;                                                          \
     } else {                                                                              \
       hipLaunchKernelGGL((k_bmm<F, true, kRmGU, 4>), ggu, dim3(256), 0, st, a);           \
