@@ -36,6 +36,10 @@
 #include "routed_fp4.h"
 #include "common.h"
 
+#ifndef RF4_PIPE_DEPTH
+#define RF4_PIPE_DEPTH 2
+#endif
+
 namespace {
 
 using namespace rf4;
@@ -772,6 +776,9 @@ struct Moe1Shared {
     float hs[kMaxI1 + kMaxI1 / 8];   // h of the slot (down)
   } u;
   SelectLds sel;                   // wave 0's selection scratch
+  uint32_t lkey[MOE_MAX_EXPERTS];  // the selection's 32-bit logit keys
+  float lval[MOE_MAX_EXPERTS];     // ... and logits
+  int ncand;
   float ys[kWG1];                  // the combining slice's own rows (R <= kWG1)
   int32_t sidx[MOE_MAX_TOPK];
   float sw[MOE_MAX_TOPK];
@@ -850,46 +857,111 @@ __device__ __forceinline__ void moe1_router_finish(const Moe1Args& a, Moe1Shared
 }
 
 // The selection, computed by every workgroup for itself from the tagged
-// logits (or taken from the caller when the selection is given).  Wave 0
-// polls one replica of the logits (expert lane + 64 i in lane, slot i) and
-// selects; the other waves wait at the closing barrier.
+// logits (or taken from the caller when the selection is given): all eight
+// waves poll and gather the candidates above a threshold, wave 0 ranks them
+// (the same exact top-k as wave_select, which remains the fallback).
 __device__ void moe1_routing(const Moe1Args& a, Moe1Shared& S, uint32_t epoch, bool writer) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int k = a.k;
   constexpr int NPL = MOE_MAX_EXPERTS / 64;
   if (a.Wr) {
-    if (wave == 0) {
-      uint64_t ck[NPL];
-      float lv[NPL];
-      const __amdgpu_buffer_rsrc_t lr = coherent_view(
-          a.tlogits + (size_t)(blockIdx.x % kLogitCopies) * a.E, (uint32_t)a.E * 8);
-      for (uint32_t it = 0;; ++it) {
-        uint2 t[NPL];
+    // Wave w polls experts e = 128 w + lane + 64 j (j < 2) of one replica.
+    const __amdgpu_buffer_rsrc_t lr = coherent_view(
+        a.tlogits + (size_t)(blockIdx.x % kLogitCopies) * a.E, (uint32_t)a.E * 8);
+    float lv[2];
+    uint32_t kv[2];
+    for (uint32_t it = 0;; ++it) {
+      uint2 t[2];
 #pragma unroll
-        for (int i = 0; i < NPL; ++i)
-          if (lane + 64 * i < a.E) t[i] = coherent_ld_u2(lr, (uint32_t)(lane + 64 * i) * 8);
-        bool missing = false;
+      for (int j = 0; j < 2; ++j) t[j] = coherent_ld_u2(lr, (uint32_t)(128 * wave + lane + 64 * j) * 8);
+      bool missing = false;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int e = 128 * wave + lane + 64 * j;
+        const bool in = e < a.E;
+        missing |= in && t[j].y != epoch;
+        lv[j] = in ? __uint_as_float(t[j].x) : 0.0f;
+        kv[j] = in ? logit_key(lv[j]) : 0u;
+      }
+      if (!wg_any(missing, &S.flag)) break;
+      if (it == kSpinLimit) {
+        if (threadIdx.x == 0)
+          __hip_atomic_store(&a.ctrl[kCtrlErr], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      S.lkey[128 * wave + lane + 64 * j] = kv[j];
+      S.lval[128 * wave + lane + 64 * j] = lv[j];
+    }
+    if (threadIdx.x == 0) S.ncand = 0;
+    __syncthreads();
+    // Every wave computes the same threshold T: with lane l holding experts
+    // l + 64 i, T is the largest t such that k lane maxima are >= t (a
+    // bit-by-bit search on the orderable 32-bit keys).  Those k lanes hold k
+    // experts with keys >= T, so every expert of the top k has a key >= T.
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+      const int e = lane + 64 * i;
+      const uint32_t kk = e < a.E ? S.lkey[e] : 0u;
+      m = kk > m ? kk : m;
+    }
+    uint32_t T = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t c = T | (1u << bit);
+      if (__popcll(__ballot(m >= c)) >= k) T = c;
+    }
+    // The candidates (keys >= T; usually a few more than k) gather in LDS,
+    // each wave adding the ones it polled.
+    bool cand[2];
+    int nmine = 0;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      cand[j] = 128 * wave + lane + 64 * j < a.E && kv[j] >= T;
+      nmine += __popcll(__ballot(cand[j]));
+    }
+    int base = 0;
+    if (lane == 0 && nmine) base = atomicAdd(&S.ncand, nmine);
+    base = __builtin_amdgcn_readfirstlane(base);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const unsigned long long bal = __ballot(cand[j]);
+      const int pos = base + __popcll(bal & ((1ull << lane) - 1ull));
+      if (cand[j] && pos < 64) {
+        const int e = 128 * wave + lane + 64 * j;
+        S.sel.cand_key[pos] = ((uint64_t)kv[j] << 32) | (uint64_t)(~(uint32_t)e);
+        S.sel.cand_l[pos] = lv[j];
+      }
+      base += __popcll(bal);
+    }
+    __syncthreads();
+    if (wave == 0) {
+      const int n = S.ncand;
+      if (n <= 64) {
+        // rank = number of candidates ahead (larger key; equal logits: lower index)
+        const uint64_t mine = lane < n ? S.sel.cand_key[lane] : 0;
+        const float ml = lane < n ? S.sel.cand_l[lane] : 0.0f;
+        int rk = 0;
+        for (int j = 0; j < n; ++j) rk += readlane_u64(mine, j) > mine ? 1 : 0;
+        if (lane < n && rk < k) {
+          S.sel.sel_e[rk] = (int32_t)~(uint32_t)mine;
+          S.sel.sel_l[rk] = ml;
+        }
+        wave_lds_fence();
+      } else {
+        // clustered winners: the general one-wave selection over all experts
+        uint64_t ck[NPL];
+        float lw[NPL];
 #pragma unroll
         for (int i = 0; i < NPL; ++i) {
           const int e = lane + 64 * i;
-          if (e < a.E) {
-            missing |= t[i].y != epoch;
-            lv[i] = __uint_as_float(t[i].x);
-            ck[i] = sel_key(lv[i], e);
-          } else {
-            lv[i] = 0.0f;
-            ck[i] = 0;
-          }
+          lw[i] = e < a.E ? S.lval[e] : 0.0f;
+          ck[i] = e < a.E ? (((uint64_t)S.lkey[e] << 32) | (uint64_t)(~(uint32_t)e)) : 0;
         }
-        if (__ballot(missing) == 0ull) break;
-        if (it == kSpinLimit) {
-          if (lane == 0)
-            __hip_atomic_store(&a.ctrl[kCtrlErr], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          break;
-        }
-        __builtin_amdgcn_s_sleep(2);
+        wave_select<NPL>(ck, lw, k, S.sel);
       }
-      wave_select<NPL>(ck, lv, k, S.sel);
       const float l = lane < k ? S.sel.sel_l[lane] : 0.0f;
       const float w = route_weight(l, lane, k);
       if (lane < k) {
@@ -954,6 +1026,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tensor_view(const uint8_t* rec
 
 constexpr int kGuStage = 4;   // chunks per lane per pipeline stage (gate/up)
 constexpr int kDnStage = 8;   // (down, one row per lane group at a time)
+constexpr int kPipe = RF4_PIPE_DEPTH;   // register buffers of the weight stream
 
 // Streamed dot products of one 16-lane group over NSEG consecutive segments
 // (segment s = NR rows, one per row stream r, at offset coff[r] + s*seg_stride);
@@ -1008,30 +1081,25 @@ struct SegStream {
       }
     }
   }
-  // all stages; stage 0 may already be loaded into q0
-  template <class Done>
-  __device__ __forceinline__ void run(const float* xs, uint4 (&q0)[PB][NR], uint32_t (&s0)[PB][NR],
-                                      bool stage0_loaded, Done done) const {
-    uint4 q1[PB][NR];
-    uint32_t s1[PB][NR];
+  // All stages, with D register buffers: the loads of stage t+D-1 are issued
+  // just before stage t is multiplied (the barriers keep the compiler from
+  // issuing them earlier, which would need more registers).  The caller may
+  // have issued stages 0..npre-1 already (into q[0..npre-1]).
+  template <int D, class Done>
+  __device__ __forceinline__ void run(const float* xs, uint4 (&q)[D][PB][NR], uint32_t (&sc)[D][PB][NR],
+                                      int npre, Done done) const {
     float acc[NR][1];
 #pragma unroll
     for (int r = 0; r < NR; ++r) acc[r][0] = 0.0f;
-    if (!stage0_loaded) load(0, q0, s0);
-    // the barriers pin the pipeline: stage t+1's loads are issued just before
-    // stage t is multiplied, never earlier (earlier would need more registers)
+#pragma unroll
+    for (int st = 0; st < D - 1; ++st)
+      if (st >= npre && st < NST) load(st, q[st], sc[st]);
 #pragma unroll
     for (int st = 0; st < NST; ++st) {
       __builtin_amdgcn_sched_barrier(0);
-      if (st & 1) {
-        if (st + 1 < NST) load(st + 1, q0, s0);
-        __builtin_amdgcn_sched_barrier(0);
-        fma(st, q1, s1, xs, acc, done);
-      } else {
-        if (st + 1 < NST) load(st + 1, q1, s1);
-        __builtin_amdgcn_sched_barrier(0);
-        fma(st, q0, s0, xs, acc, done);
-      }
+      if (st + D - 1 < NST) load(st + D - 1, q[(st + D - 1) % D], sc[(st + D - 1) % D]);
+      __builtin_amdgcn_sched_barrier(0);
+      fma(st, q[st % D], sc[st % D], xs, acc, done);
     }
   }
 };
@@ -1069,9 +1137,9 @@ __device__ void moe1_gate_up_slice(const Moe1Args& a, Moe1Shared& S, int u, int 
     const float usum = group16_sum(acc[1][0]);
     if (l16 == 0) store_tagged(&hout[row0 + (kWG1 / 16) * sg], epoch, silu(gg * gsum) * (gu * usum));
   };
-  uint4 q0[kGuStage][2];
-  uint32_t s0[kGuStage][2];
-  ss.run(S.u.xs, q0, s0, false, done);
+  uint4 q[kPipe][kGuStage][2];
+  uint32_t sc[kPipe][kGuStage][2];
+  ss.template run<kPipe>(S.u.xs, q, sc, 0, done);
 }
 
 // Down slice: rows b*R + lg + 16*s (within the block of R = H / workgroups per
@@ -1097,9 +1165,10 @@ __device__ void moe1_down_slice(const Moe1Args& a, Moe1Shared& S, int u, int b, 
     ss.soff[0] = (uint32_t)row0 * (I / B) + l16 * (32 / B);
     ss.seg_stride = (kWG1 / 16) * (uint32_t)(I / 2);
     ss.seg_sstride = (kWG1 / 16) * (uint32_t)(I / B);
-    uint4 q0[kDnStage][1];
-    uint32_t s0[kDnStage][1];
-    ss.load(0, q0, s0);
+    uint4 q[kPipe][kDnStage][1];
+    uint32_t sc[kPipe][kDnStage][1];
+#pragma unroll
+    for (int st = 0; st < kPipe - 1; ++st) ss.load(st, q[st], sc[st]);
     // the first weights are in flight; now fetch this slot's h (polling until
     // every value carries this call's epoch) into LDS, over the dead x stage
     __syncthreads();
@@ -1143,7 +1212,7 @@ __device__ void moe1_down_slice(const Moe1Args& a, Moe1Shared& S, int u, int b, 
         else store_tagged(&a.tpart[(size_t)u * H + j], epoch, y);
       }
     };
-    ss.run(S.u.hs, q0, s0, true, done);
+    ss.template run<kPipe>(S.u.hs, q, sc, kPipe - 1, done);
   }
   if (!combiner) return;
   // the last slot's workgroups add the k slot results of their rows in order
