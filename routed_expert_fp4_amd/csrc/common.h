@@ -58,7 +58,7 @@ inline WsLayout ws_layout(int E, int H, int I, int k, int C) {
   L.h = o;      o = align256(o + (decode ? CK * I * sizeof(float) : 0));
   L.part = o;   o = align256(o + CK * H * sizeof(float));
   // batch-1 kernel: (epoch, value) words
-  L.tlogits = o; o = align256(o + (size_t)kLogitCopies * E * sizeof(uint64_t));
+  L.tlogits = o; o = align256(o + (size_t)kLogitCopies * 2 * E * sizeof(uint64_t));
   L.th = o;      o = align256(o + (size_t)k * I * sizeof(uint64_t));
   L.tpart = o;   o = align256(o + (size_t)k * H * sizeof(uint64_t));
   // batched path

@@ -782,7 +782,6 @@ struct Moe1Shared {
   float ys[kWG1];                  // the combining slice's own rows (R <= kWG1)
   int32_t sidx[MOE_MAX_TOPK];
   float sw[MOE_MAX_TOPK];
-  float red[8];
   int flag;
 };
 
@@ -794,21 +793,28 @@ __device__ __forceinline__ bool wg_any(bool v, int* s_flag) {
   return *s_flag != 0;
 }
 
-// Router rows e0, e0 + kG1, e0 + 2*kG1, e0 + 3*kG1 (those below E) at once:
-// wave w takes half (w & 1) of row w >> 1, so every weight load of the four
-// rows is in flight together; the two halves are added in a fixed order and
-// the logit is written, tagged, to every replica.  The loads are issued
-// first (moe1_router_load) so they can be in flight while x is staged.
+// Router: the 2E half rows of W_r are spread evenly, hpw = ceil(2E / kG1) <= 8
+// per workgroup, one per wave: wave w of workgroup g takes half row
+// hr = g * hpw + w (row hr / 2, columns (hr & 1) * H/2 .. +H/2).  Each half's
+// dot product goes out, tagged, to every replica; the selection adds the two
+// halves of a row in a fixed order.  The loads are issued first
+// (moe1_router_load) so they can be in flight while x is staged.
 constexpr int kRouterRU = kMaxH1 / 2 / 4 / 64;     // float4 loads per lane (max)
 
-__device__ __forceinline__ void moe1_router_load(const Moe1Args& a, int e0, float4 (&wv)[kRouterRU]) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int r = wave >> 1, half = wave & 1;
-  const int e = e0 + r * kG1;
-  const int q = a.H / 2;                          // this wave's half of K
+__device__ __forceinline__ int router_half_row(const Moe1Args& a) {
+  const int hpw = (2 * a.n_router + kG1 - 1) / kG1;
+  const int wave = threadIdx.x >> 6;
+  const int hr = blockIdx.x * hpw + wave;
+  return (wave < hpw && hr < 2 * a.n_router) ? hr : -1;
+}
+
+__device__ __forceinline__ void moe1_router_load(const Moe1Args& a, int hr, float4 (&wv)[kRouterRU]) {
+  const int lane = threadIdx.x & 63;
+  const int q = a.H / 2;                          // columns per half row
 #pragma unroll
   for (int u = 0; u < kRouterRU; ++u) wv[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (e < a.E) {
+  if (hr >= 0) {
+    const int e = hr >> 1, half = hr & 1;
     const __amdgpu_buffer_rsrc_t wr =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(a.Wr + (size_t)e * a.H), (short)0,
                                           a.H * 4, 0x00020000);
@@ -826,34 +832,24 @@ __device__ __forceinline__ void moe1_router_load(const Moe1Args& a, int e0, floa
   }
 }
 
-__device__ __forceinline__ void moe1_router_finish(const Moe1Args& a, Moe1Shared& S, int e0,
-                                   const float4 (&wv)[kRouterRU], uint32_t epoch) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int r = wave >> 1, half = wave & 1;
-  const int e = e0 + r * kG1;
+__device__ __forceinline__ void moe1_router_finish(const Moe1Args& a, Moe1Shared& S, int hr,
+                                                   const float4 (&wv)[kRouterRU], uint32_t epoch) {
+  const int lane = threadIdx.x & 63;
   const int q = a.H / 2;
+  if (hr < 0) return;                             // whole waves
+  const int e = hr >> 1, half = hr & 1;
   float acc = 0.0f;
-  if (e < a.E) {
 #pragma unroll
-    for (int u = 0; u < kRouterRU; ++u) {
-      const int c = (lane + 64 * u) * 4;
-      if (c < q) {
-        const int col = half * q + c;
-        const float4 xv = *reinterpret_cast<const float4*>(&S.u.xs[col + (col >> 5) * 4]);
-        acc += wv[u].x * xv.x + wv[u].y * xv.y + wv[u].z * xv.z + wv[u].w * xv.w;
-      }
+  for (int u = 0; u < kRouterRU; ++u) {
+    const int c = (lane + 64 * u) * 4;
+    if (c < q) {
+      const int col = half * q + c;
+      const float4 xv = *reinterpret_cast<const float4*>(&S.u.xs[col + (col >> 5) * 4]);
+      acc += wv[u].x * xv.x + wv[u].y * xv.y + wv[u].z * xv.z + wv[u].w * xv.w;
     }
   }
   acc = wave_sum(acc);
-  if (lane == 0) S.red[wave] = acc;
-  __syncthreads();
-  if (threadIdx.x < 4 * kLogitCopies) {
-    const int rr = threadIdx.x / kLogitCopies, copy = threadIdx.x % kLogitCopies;
-    const int er = e0 + rr * kG1;
-    if (er < a.E)
-      store_tagged(&a.tlogits[(size_t)copy * a.E + er], epoch, S.red[2 * rr] + S.red[2 * rr + 1]);
-  }
-  __syncthreads();
+  if (lane < kLogitCopies) store_tagged(&a.tlogits[(size_t)lane * 2 * a.E + 2 * e + half], epoch, acc);
 }
 
 // The selection, computed by every workgroup for itself from the tagged
@@ -867,20 +863,20 @@ __device__ void moe1_routing(const Moe1Args& a, Moe1Shared& S, uint32_t epoch, b
   if (a.Wr) {
     // Wave w polls experts e = 128 w + lane + 64 j (j < 2) of one replica.
     const __amdgpu_buffer_rsrc_t lr = coherent_view(
-        a.tlogits + (size_t)(blockIdx.x % kLogitCopies) * a.E, (uint32_t)a.E * 8);
+        a.tlogits + (size_t)(blockIdx.x % kLogitCopies) * 2 * a.E, (uint32_t)a.E * 16);
     float lv[2];
     uint32_t kv[2];
     for (uint32_t it = 0;; ++it) {
-      uint2 t[2];
+      uint4 t[2];                                // {half 0, tag, half 1, tag}
 #pragma unroll
-      for (int j = 0; j < 2; ++j) t[j] = coherent_ld_u2(lr, (uint32_t)(128 * wave + lane + 64 * j) * 8);
+      for (int j = 0; j < 2; ++j) t[j] = coherent_ld_u4(lr, (uint32_t)(128 * wave + lane + 64 * j) * 16);
       bool missing = false;
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int e = 128 * wave + lane + 64 * j;
         const bool in = e < a.E;
-        missing |= in && t[j].y != epoch;
-        lv[j] = in ? __uint_as_float(t[j].x) : 0.0f;
+        missing |= in && (t[j].y != epoch || t[j].w != epoch);
+        lv[j] = in ? __uint_as_float(t[j].x) + __uint_as_float(t[j].z) : 0.0f;
         kv[j] = in ? logit_key(lv[j]) : 0u;
       }
       if (!wg_any(missing, &S.flag)) break;
@@ -1275,18 +1271,15 @@ __global__ __launch_bounds__(kWG1, 1) void k_moe1(Moe1Args a) {
   __shared__ Moe1Shared S;
   const int tid = threadIdx.x;
   float4 wv[kRouterRU];
-  int e0 = blockIdx.x;
-  if (e0 < a.n_router) moe1_router_load(a, e0, wv);     // in flight while x is staged
+  const int hr = router_half_row(a);
+  moe1_router_load(a, hr, wv);                          // in flight while x is staged
   // x stays in LDS through the gate/up slice
   for (int i = tid * 4; i < a.H; i += kWG1 * 4)
     *reinterpret_cast<float4*>(&S.u.xs[i + (i >> 5) * 4]) = *reinterpret_cast<const float4*>(a.x + i);
   const uint32_t epoch =
       __hip_atomic_load(&a.ctrl[kCtrlEpoch], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
   __syncthreads();
-  for (; e0 < a.n_router; e0 += 4 * gridDim.x) {
-    if (e0 != (int)blockIdx.x) moe1_router_load(a, e0, wv);
-    moe1_router_finish(a, S, e0, wv, epoch);
-  }
+  moe1_router_finish(a, S, hr, wv, epoch);
   moe1_routing(a, S, epoch, blockIdx.x == 0);
   const int wpe = gridDim.x / a.k;               // workgroups per slot
   const int u = blockIdx.x / wpe, b = blockIdx.x - u * wpe;
