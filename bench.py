@@ -68,7 +68,8 @@ def calibrate_copy():
     log(f"copied {n} bytes x 3")
 
 
-KERNEL_SRC = os.path.join(ROOT, "routed_expert_fp4_amd", "csrc", "routed_fp4.hip")
+KERNEL_SRC = tuple(os.path.join(ROOT, "routed_expert_fp4_amd", "csrc", f)
+                   for f in ("routed_fp4.hip", "common.h"))
 COUNTERS = os.path.join(ROOT, "profiles", "k_moe1_k3_stack_nvfp4_hbm_counters.md")
 
 
@@ -90,12 +91,13 @@ def measured_traffic():
     return int(t.group(1))
 
 
-def code_sha256(path: str) -> str:
-    """sha256 of a C/HIP source with comments and blank space removed, so an
-    edit to comments alone does not void measurements of the same code."""
+def code_sha256(paths) -> str:
+    """sha256 of C/HIP sources (concatenated in the given order) with comments
+    and blank space removed, so an edit to comments alone does not void
+    measurements of the same code."""
     import hashlib
     import re
-    text = open(path).read()
+    text = "".join(open(p).read() for p in paths)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     text = re.sub(r"//[^\n]*", "", text)
     text = "\n".join(line.strip() for line in text.splitlines() if line.strip())
