@@ -546,9 +546,12 @@ __global__ __launch_bounds__(256) void k_brouter(const float* x, const float* Wr
 }
 
 // One wave per token: the decode path's exact top-k and renormalised sigmoid
-// weights.
-__global__ __launch_bounds__(512) void k_btopk(const float* logits, int C, int E, int k,
-                                               int32_t* idx, float* w) {
+// weights.  The logits are given, or are the sums of ksplit partial sums
+// lpart[s][t][e], added in split order (and then stored to logits_out if
+// that is not null).
+__global__ __launch_bounds__(512) void k_btopk(const float* logits, const float* lpart, int ksplit,
+                                               float* logits_out, int C, int E, int k, int32_t* idx,
+                                               float* w) {
   __shared__ SelectLds S[8];
   constexpr int NPL = MOE_MAX_EXPERTS / 64;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -559,7 +562,17 @@ __global__ __launch_bounds__(512) void k_btopk(const float* logits, int C, int E
 #pragma unroll
   for (int i = 0; i < NPL; ++i) {
     const int e = lane + 64 * i;
-    lv[i] = e < E ? logits[(size_t)t * E + e] : 0.0f;
+    float l = 0.0f;
+    if (e < E) {
+      if (lpart) {
+        l = lpart[(size_t)t * E + e];
+        for (int s = 1; s < ksplit; ++s) l += lpart[((size_t)s * C + t) * E + e];
+        if (logits_out) logits_out[(size_t)t * E + e] = l;
+      } else {
+        l = logits[(size_t)t * E + e];
+      }
+    }
+    lv[i] = l;
     ck[i] = e < E ? sel_key(lv[i], e) : 0;
   }
   wave_select<NPL>(ck, lv, k, S[wave]);
@@ -828,7 +841,15 @@ moe_status launch_batched_route(const float* x, const float* Wr, const float* lo
                        C, H, E);
     lg = dst;
   }
-  hipLaunchKernelGGL(k_btopk, dim3((C + 7) / 8), dim3(512), 0, st, lg, C, E, k, idx, w);
+  hipLaunchKernelGGL(k_btopk, dim3((C + 7) / 8), dim3(512), 0, st, lg, nullptr, 0, nullptr, C, E, k,
+                     idx, w);
+  return status_of_launch();
+}
+
+moe_status launch_topk_parts(const float* lpart, int ksplit, float* logits_out, int C, int E, int k,
+                             int32_t* idx, float* w, hipStream_t st) {
+  hipLaunchKernelGGL(k_btopk, dim3((C + 7) / 8), dim3(512), 0, st, nullptr, lpart, ksplit,
+                     logits_out, C, E, k, idx, w);
   return status_of_launch();
 }
 

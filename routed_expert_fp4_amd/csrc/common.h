@@ -48,7 +48,7 @@ inline WsLayout ws_layout(int E, int H, int I, int k, int C) {
   size_t o = 0;
   const size_t CK = (size_t)C * k;
   const bool decode = C <= MOE_MAX_DECODE_TOKENS;   // the split-K router path
-  L.ctrl = o;   o = align256(o + 64 * sizeof(uint32_t));
+  L.ctrl = o;   o = align256(o + (64 + 256) * sizeof(uint32_t));   // control words, arrival words
   L.dtick = o;  o = align256(o + (size_t)((H + kDnRows - 1) / kDnRows) * sizeof(uint32_t));
   L.lpart = o;  o = align256(o + (decode ? (size_t)kKsplitMax * C * E * sizeof(float) : 0));
   L.logits = o; o = align256(o + (size_t)C * E * sizeof(float));
@@ -59,7 +59,7 @@ inline WsLayout ws_layout(int E, int H, int I, int k, int C) {
   L.part = o;   o = align256(o + CK * H * sizeof(float));
   // batch-1 kernel: (epoch, value) words
   L.tlogits = o; o = align256(o + (size_t)kLogitCopies * 2 * E * sizeof(uint64_t));
-  L.th = o;      o = align256(o + (size_t)k * I * sizeof(uint64_t));
+  L.th = o;      o = align256(o + 2 * (size_t)k * I * sizeof(uint64_t));   // XCD copy, coherent copy
   L.tpart = o;   o = align256(o + (size_t)k * H * sizeof(uint64_t));
   // batched path
   L.bcount = o;  o = align256(o + (size_t)E * sizeof(uint32_t));
@@ -309,6 +309,11 @@ inline bool batched_shape_ok(const moe_bank* b) {
 moe_status launch_batched_route(const float* x, const float* Wr, const float* logits_in,
                                 float* logits_out, int C, int H, int E, int k, int32_t* idx,
                                 float* w, uint8_t* ws, const WsLayout& L, hipStream_t st);
+// launch_topk_parts: the top-k of C tokens (one wave each) from ksplit
+// partial router sums lpart[s][t][e], added in split order; the logits go to
+// logits_out too when it is not null.
+moe_status launch_topk_parts(const float* lpart, int ksplit, float* logits_out, int C, int E, int k,
+                             int32_t* idx, float* w, hipStream_t st);
 // launch_batched_experts: the selected experts of C tokens as grouped GEMMs
 // on the matrix cores, then the fixed-order combine into out.
 moe_status launch_batched_experts(const moe_bank* b, const float* x, int C, int k,

@@ -58,6 +58,7 @@ struct RouteArgs {
   uint32_t* ctrl;          // ctrl[0]: router ticket
   int32_t* disp;           // dispatch table or null
   int C, H, E, k, ksplit, kper;
+  int select;              // 0: the split-K sums are left for k_btopk (several tokens)
 };
 
 struct TopkShared {
@@ -236,24 +237,40 @@ __device__ void topk_token(const RouteArgs& a, TopkShared& S, int t, bool active
   const int E = a.E, k = a.k;
   uint32_t key[16];
   float lv[16];
+  if (a.x) {
+    // every split-K partial of the lane's 16 experts in flight at once (loads
+    // outside the view read zeros), then added in split order
+    const __amdgpu_buffer_rsrc_t lp =
+        coherent_view(a.lpart, (uint32_t)((size_t)a.ksplit * a.C * E * sizeof(float)));
+    float pv[kKsplitMax][16];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int e = lane + 64 * i;
-    float l = 0.0f;
-    if (active && e < E) {
-      if (a.x) {
-        const __amdgpu_buffer_rsrc_t lp =
-            coherent_view(a.lpart, (uint32_t)((size_t)a.ksplit * a.C * E * sizeof(float)));
-        l = coherent_ld(lp, (uint32_t)(((size_t)t * E + e) * 4));
-        for (int s = 1; s < a.ksplit; ++s)
-          l += coherent_ld(lp, (uint32_t)((((size_t)s * a.C + t) * E + e) * 4));
-        if (a.logits_out) a.logits_out[(size_t)t * E + e] = l;
-      } else {
-        l = a.logits_in[(size_t)t * E + e];
+    for (int s = 0; s < kKsplitMax; ++s)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int e = lane + 64 * i;
+        const bool in = active && e < E && s < a.ksplit;
+        pv[s][i] = coherent_ld(lp, in ? (uint32_t)((((size_t)s * a.C + t) * E + e) * 4) : 0x80000000u);
       }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float l = pv[0][i];
+#pragma unroll
+      for (int s = 1; s < kKsplitMax; ++s)
+        if (s < a.ksplit) l += pv[s][i];
+      const int e = lane + 64 * i;
+      if (!(active && e < E)) l = 0.0f;
+      else if (a.logits_out) a.logits_out[(size_t)t * E + e] = l;
+      lv[i] = l;
+      key[i] = logit_key(l);
     }
-    lv[i] = l;
-    key[i] = logit_key(l);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int e = lane + 64 * i;
+      const float l = (active && e < E) ? a.logits_in[(size_t)t * E + e] : 0.0f;
+      lv[i] = l;
+      key[i] = logit_key(l);
+    }
   }
   wave_topk(S, key, lv, E, k, active);
   if (active) {
@@ -373,8 +390,9 @@ __global__ __launch_bounds__(kWG) void k_route(RouteArgs a) {
         if (lane == 0 && e < a.E) store_coherent(&a.lpart[((size_t)ks * a.C + t) * a.E + e], v);
       }
     }
-    // the last workgroup to finish runs the selection
-    if (!last_to_arrive(&a.ctrl[0], gridDim.x, &s_last)) return;
+    // the last workgroup to finish runs the selection (or a separate launch
+    // selects, one wave per token)
+    if (!a.select || !last_to_arrive(&a.ctrl[0], gridDim.x, &s_last)) return;
   }
   for (int t0 = 0; t0 < a.C; t0 += 4) topk_token(a, S, t0 + wave, t0 + wave < a.C);
   __syncthreads();
@@ -708,13 +726,16 @@ __global__ void k_zero_uncovered(ExpArgs a) {
 // Hand-offs between workgroups carry the call's epoch: a producer writes
 // (epoch, value) as one 64-bit agent-coherent store and moves on; a consumer
 // polls until every value it needs carries the current epoch.  No producer
-// ever waits for its stores and no work item takes a ticket.  The last
-// workgroup to exit advances the epoch for the next call.
-enum { kCtrlRouteTicket = 0, kCtrlExit = 3, kCtrlErr = 4, kCtrlEpoch = 5 };
+// ever waits for its stores and no work item takes a ticket.  Every
+// workgroup writes an arrival word once it has read the epoch; one workgroup
+// of the combine publishes the next epoch after seeing all of them.
+enum { kCtrlRouteTicket = 0, kCtrlErr = 4, kCtrlEpoch = 5, kCtrlArrive = 64 };
 constexpr int kG1 = 256;                  // workgroups of the batch-1 kernel (one per CU)
 constexpr int kWG1 = 512;                 // threads per batch-1 workgroup (8 waves)
 constexpr int kMaxH1 = 8192;              // batch-1 kernel limits
 constexpr int kMaxI1 = 4096;
+constexpr int kXcds = 8;                   // XCDs; workgroup w is dispatched to XCD w % 8
+constexpr uint32_t kXcdPolls = 256;       // XCD-copy polls before the coherent copy
 constexpr uint32_t kSpinLimit = 1u << 22; // ~seconds: a wait that never ends gives up
 
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
@@ -741,6 +762,13 @@ __device__ __forceinline__ void store_tagged(uint64_t* p, uint32_t epoch, float 
   __hip_atomic_store(p, ((uint64_t)epoch << 32) | __float_as_uint(v), __ATOMIC_RELAXED,
                      __HIP_MEMORY_SCOPE_AGENT);
 }
+// The same word for readers on this XCD only: it stays in the XCD's L2, where
+// their coherent loads find it at L2 latency instead of a memory round trip
+// behind the weight stream.
+__device__ __forceinline__ void store_tagged_xcd(uint64_t* p, uint32_t epoch, float v) {
+  __hip_atomic_store(p, ((uint64_t)epoch << 32) | __float_as_uint(v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_WORKGROUP);
+}
 // two tagged words with one 16-byte coherent load: {lo0, epoch0, lo1, epoch1}
 __device__ __forceinline__ uint4 coherent_ld_u4(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
   const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, kCachePolicySc1);
@@ -763,7 +791,7 @@ struct Moe1Args {
   int32_t* idx_out;        // [k] or null
   float* w_out;            // [k] or null
   uint64_t* tlogits;       // ws [E]      tagged router logits
-  uint64_t* th;            // ws [k][I]   tagged intermediate activations
+  uint64_t* th;            // ws [2][k][I] tagged intermediate activations: XCD copy, coherent copy
   uint64_t* tpart;         // ws [k][H]   tagged per-slot down outputs
   float* out;              // [H]
   uint32_t* ctrl;
@@ -808,27 +836,24 @@ __device__ __forceinline__ int router_half_row(const Moe1Args& a) {
   return (wave < hpw && hr < 2 * a.n_router) ? hr : -1;
 }
 
+// Every load is issued (those past the half row, or of a wave without one,
+// fall outside the view and read zeros), so the loads form one straight run
+// and later waits can count them exactly.
 __device__ __forceinline__ void moe1_router_load(const Moe1Args& a, int hr, float4 (&wv)[kRouterRU]) {
   const int lane = threadIdx.x & 63;
   const int q = a.H / 2;                          // columns per half row
+  const int e = hr >= 0 ? hr >> 1 : 0, half = hr & 1;
+  const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(hr >= 0 ? a.Wr + (size_t)e * a.H : a.x), (short)0, hr >= 0 ? a.H * 4 : 0,
+      0x00020000);
+  const uint32_t woff = (uint32_t)(half * q + lane * 4) * 4;
 #pragma unroll
-  for (int u = 0; u < kRouterRU; ++u) wv[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (hr >= 0) {
-    const int e = hr >> 1, half = hr & 1;
-    const __amdgpu_buffer_rsrc_t wr =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(a.Wr + (size_t)e * a.H), (short)0,
-                                          a.H * 4, 0x00020000);
-    const uint32_t woff = (uint32_t)(half * q + lane * 4) * 4;
-#pragma unroll
-    for (int u = 0; u < kRouterRU; ++u) {
-      const int c = (lane + 64 * u) * 4;
-      if (c < q) {
-        const auto v = __builtin_amdgcn_raw_buffer_load_b128(wr, (int)(woff + 1024 * u), 0,
-                                                             kCachePolicyNt);
-        wv[u] = make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]),
-                            __uint_as_float(v[3]));
-      }
-    }
+  for (int u = 0; u < kRouterRU; ++u) {
+    const int c = (lane + 64 * u) * 4;
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(
+        wr, (int)(c < q ? woff + 1024 * u : 0x80000000u), 0, kCachePolicyNt);
+    wv[u] = make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]),
+                        __uint_as_float(v[3]));
   }
 }
 
@@ -1128,10 +1153,16 @@ __device__ void moe1_gate_up_slice(const Moe1Args& a, Moe1Shared& S, int u, int 
     gu = g[1];
   }
   uint64_t* hout = a.th + (size_t)u * I;
+  uint64_t* hcoh = hout + (size_t)a.k * I;
   auto done = [&](int sg, float (&acc)[2][1]) {
     const float gsum = group16_sum(acc[0][0]);
     const float usum = group16_sum(acc[1][0]);
-    if (l16 == 0) store_tagged(&hout[row0 + (kWG1 / 16) * sg], epoch, silu(gg * gsum) * (gu * usum));
+    if (l16 == 0) {
+      const int j = row0 + (kWG1 / 16) * sg;
+      const float h = silu(gg * gsum) * (gu * usum);
+      store_tagged_xcd(&hout[j], epoch, h);
+      store_tagged(&hcoh[j], epoch, h);
+    }
   };
   uint4 q[kPipe][kGuStage][2];
   uint32_t sc[kPipe][kGuStage][2];
@@ -1143,7 +1174,7 @@ __device__ void moe1_gate_up_slice(const Moe1Args& a, Moe1Shared& S, int u, int 
 // or, for the last slot, to LDS for the combine.
 template <int FMT, int KD, int SDN, int KT>
 __device__ void moe1_down_slice(const Moe1Args& a, Moe1Shared& S, int u, int b, int R,
-                                uint32_t epoch) {
+                                uint32_t epoch, bool xcd_local) {
   const int e = S.sidx[u];
   const bool valid = e >= 0 && e < a.E;
   const bool combiner = (u == a.k - 1);
@@ -1169,9 +1200,15 @@ __device__ void moe1_down_slice(const Moe1Args& a, Moe1Shared& S, int u, int b, 
     // every value carries this call's epoch) into LDS, over the dead x stage
     __syncthreads();
     {
-      const __amdgpu_buffer_rsrc_t hv = coherent_view(a.th + (size_t)u * I, (uint32_t)I * 8);
+      // The slot's workgroups share this XCD (see k_moe1), so h is read from
+      // the XCD copy, which stays in its L2.  Should they not (another
+      // dispatch order), the XCD copy never arrives here and the polls move to
+      // the coherent copy after kXcdPolls tries.
+      const __amdgpu_buffer_rsrc_t hx = coherent_view(a.th + (size_t)u * I, (uint32_t)I * 8);
+      const __amdgpu_buffer_rsrc_t hc = coherent_view(a.th + (size_t)(a.k + u) * I, (uint32_t)I * 8);
       constexpr int NP = (KD * 512 / 2 + kWG1 - 1) / kWG1;   // 16-byte pairs per thread
       for (uint32_t it = 0;; ++it) {
+        const __amdgpu_buffer_rsrc_t hv = (xcd_local && it < kXcdPolls) ? hx : hc;
         bool missing = false;
         uint4 t[NP];
 #pragma unroll
@@ -1248,6 +1285,25 @@ __device__ void moe1_down_slice(const Moe1Args& a, Moe1Shared& S, int u, int b, 
       a.out[j] = acc;
     }
   }
+  // Once every workgroup has read this call's epoch (its arrival word), the
+  // next call's can be published; the words were written at the start, so
+  // the first poll normally sees them all.
+  if (b == 0) {
+    const __amdgpu_buffer_rsrc_t av = coherent_view(&a.ctrl[kCtrlArrive], kG1 * 4);
+    for (uint32_t it = 0;; ++it) {
+      const bool missing =
+          threadIdx.x < kG1 && __float_as_uint(coherent_ld(av, threadIdx.x * 4)) != epoch;
+      if (!wg_any(missing, &S.flag)) break;
+      if (it == kSpinLimit) {
+        if (threadIdx.x == 0)
+          __hip_atomic_store(&a.ctrl[kCtrlErr], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+    if (threadIdx.x == 0)
+      __hip_atomic_store(&a.ctrl[kCtrlEpoch], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 // The whole layer for one token, under a cooperative launch of kG1
@@ -1270,28 +1326,51 @@ template <int FMT, int KG, int KD, int SGU, int SDN, int KT>
 __global__ __launch_bounds__(kWG1, 1) void k_moe1(Moe1Args a) {
   __shared__ Moe1Shared S;
   const int tid = threadIdx.x;
-  float4 wv[kRouterRU];
-  const int hr = router_half_row(a);
-  moe1_router_load(a, hr, wv);                          // in flight while x is staged
-  // x stays in LDS through the gate/up slice
-  for (int i = tid * 4; i < a.H; i += kWG1 * 4)
-    *reinterpret_cast<float4*>(&S.u.xs[i + (i >> 5) * 4]) = *reinterpret_cast<const float4*>(a.x + i);
+  // the epoch first, ahead of the router stream in this CU's memory queue
   const uint32_t epoch =
       __hip_atomic_load(&a.ctrl[kCtrlEpoch], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+  // x next, then the router rows; x goes to LDS (where it stays through the
+  // gate/up slice) as soon as its own loads are in, while the rows stream
+  constexpr int kXv = kMaxH1 / (kWG1 * 4);              // float4 of x per thread
+  float4 xv[kXv];
+#pragma unroll
+  for (int j = 0; j < kXv; ++j) {
+    const int i = (tid + j * kWG1) * 4;
+    xv[j] = i < a.H ? *reinterpret_cast<const float4*>(a.x + i) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  float4 wv[kRouterRU];
+  const int hr = router_half_row(a);
+  moe1_router_load(a, hr, wv);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int j = 0; j < kXv; ++j) {
+    const int i = (tid + j * kWG1) * 4;
+    if (i < a.H) *reinterpret_cast<float4*>(&S.u.xs[i + (i >> 5) * 4]) = xv[j];
+  }
+  // this workgroup has read the epoch (the combine waits for all of these
+  // before it publishes the next one)
+  if (tid == 0)
+    __hip_atomic_store(&a.ctrl[kCtrlArrive + blockIdx.x], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   moe1_router_finish(a, S, hr, wv, epoch);
   moe1_routing(a, S, epoch, blockIdx.x == 0);
+  // Slot u's wpe workgroups: with k a multiple of kXcds they all run on one
+  // XCD (workgroup w is dispatched to XCD w % kXcds), which keeps the h
+  // hand-off between them in that XCD's L2.
   const int wpe = gridDim.x / a.k;               // workgroups per slot
-  const int u = blockIdx.x / wpe, b = blockIdx.x - u * wpe;
-  moe1_gate_up_slice<FMT, KG, SGU>(a, S, u, b, epoch);
-  moe1_down_slice<FMT, KD, SDN, KT>(a, S, u, b, a.H / wpe, epoch);
-  // the last workgroup out advances the epoch for the next call
-  if (tid == 0 &&
-      __hip_atomic_fetch_add(&a.ctrl[kCtrlExit], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-          gridDim.x - 1) {
-    __hip_atomic_store(&a.ctrl[kCtrlEpoch], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    reset_ticket(&a.ctrl[kCtrlExit]);
+  const bool xcd_local = a.k % kXcds == 0;
+  int u, b;
+  if (xcd_local) {
+    const int x = blockIdx.x % kXcds, r = blockIdx.x / kXcds;
+    u = x * (a.k / kXcds) + r / wpe;
+    b = r % wpe;
+  } else {
+    u = blockIdx.x / wpe;
+    b = blockIdx.x - u * wpe;
   }
+  moe1_gate_up_slice<FMT, KG, SGU>(a, S, u, b, epoch);
+  moe1_down_slice<FMT, KD, SDN, KT>(a, S, u, b, a.H / wpe, epoch, xcd_local);
 }
 
 // ---------------------------------------------------------------------------
@@ -1424,10 +1503,15 @@ moe_status launch_route(const float* x, const float* Wr, const float* logits_in,
     a.ksplit = 1;
     a.kper = H;
   }
+  // Several tokens and no dispatch table: the top-k runs as its own launch,
+  // one wave per token, instead of token after token in the last workgroup.
+  a.select = (x && C > 1 && !disp) ? 0 : 1;
   if (C == 1) hipLaunchKernelGGL(k_route<1>, dim3(grid), dim3(kWG), 0, st, a);
   else if (C <= 4) hipLaunchKernelGGL(k_route<4>, dim3(grid), dim3(kWG), 0, st, a);
   else hipLaunchKernelGGL(k_route<16>, dim3(grid), dim3(kWG), 0, st, a);
-  return launch_status();
+  moe_status s = launch_status();
+  if (s == MOE_OK && !a.select) s = launch_topk_parts(a.lpart, a.ksplit, logits_out, C, E, k, idx, w, st);
+  return s;
 }
 
 moe_status launch_experts(const moe_bank* b, const float* x, int C, int k, const int32_t* idx,
