@@ -26,9 +26,9 @@
 //   k_bscan     offsets and the tile list (each expert's pairs in tiles of
 //               16 or 64)
 //   k_bscatter  pairs grouped by expert
-//   k_bmm<GU>   per (tile, 128 rows of I): gate and up on MFMA, SwiGLU, h as
+//   k_bmm<GU>   per (tile, 64 rows of I): gate and up on MFMA, SwiGLU, h as
 //               two bf16 planes
-//   k_bmm<DN>   per (tile, 256 rows of H): down on MFMA, times the routing
+//   k_bmm<DN>   per (tile, 128 rows of H): down on MFMA, times the routing
 //               weight, one fp32 row per pair
 //   k_bcombine  out[t] = sum of its pairs' rows in slot order (deterministic)
 // and for the router of many tokens:
@@ -43,8 +43,8 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kRmGU = 2;             // gate/up: 16-row MFMA tiles per wave (128 rows per workgroup)
-constexpr int kRmDN = 4;             // down: 16-row MFMA tiles per wave (256 rows per workgroup)
+constexpr int kRmGU = 1;             // gate/up: 16-row MFMA tiles per wave (64 rows per workgroup)
+constexpr int kRmDN = 2;             // down: 16-row MFMA tiles per wave (128 rows per workgroup)
 constexpr int kRmGUn = 2;            // narrow tiles: gate/up 128 rows per workgroup
 constexpr int kRmDNn = 4;            // narrow tiles: down 256 rows per workgroup
 constexpr int kRK = 32;              // router: K elements per staged chunk
