@@ -807,7 +807,7 @@ struct Moe1Shared {
   uint32_t lkey[MOE_MAX_EXPERTS];  // the selection's 32-bit logit keys
   float lval[MOE_MAX_EXPERTS];     // ... and logits
   int ncand;
-  float ys[kWG1];                  // the combining slice's own rows (R <= kWG1)
+  float ys[kWG1];                  // the combine's slot results [k][H / kG1]
   int32_t sidx[MOE_MAX_TOPK];
   float sw[MOE_MAX_TOPK];
   int flag;
@@ -1177,7 +1177,6 @@ __device__ void moe1_down_slice(const Moe1Args& a, Moe1Shared& S, int u, int b, 
                                 uint32_t epoch, bool xcd_local) {
   const int e = S.sidx[u];
   const bool valid = e >= 0 && e < a.E;
-  const bool combiner = (u == a.k - 1);
   const int lg = threadIdx.x >> 4, l16 = threadIdx.x & 15;
   const int H = a.H, I = a.I;
   const int B = (FMT == MOE_FMT_MXFP4) ? 32 : 16;
@@ -1240,83 +1239,74 @@ __device__ void moe1_down_slice(const Moe1Args& a, Moe1Shared& S, int u, int b, 
     auto done = [&](int sg, float (&acc)[1][1]) {
       const float y = wgt * group16_sum(acc[0][0]);
       const int rl = lg + (kWG1 / 16) * sg, j = b * R + rl;
-      if (l16 == 0 && rl < R && j < H) {
-        if (combiner) S.ys[rl] = y;
-        else store_tagged(&a.tpart[(size_t)u * H + j], epoch, y);
-      }
+      if (l16 == 0 && rl < R && j < H) store_tagged(&a.tpart[(size_t)u * H + j], epoch, y);
     };
     ss.template run<kPipe>(S.u.hs, q, sc, kPipe - 1, done);
   }
-  if (!combiner) return;
-  // the last slot's workgroups add the k slot results of their rows in order
-  // (all k - 1 loads of a row in flight at once)
-  __syncthreads();
+}
+
+// The combine: workgroup g adds the k slot results of rows g * RC .. g * RC +
+// RC - 1 (RC = H / kG1) in slot order, one tagged word per thread in flight
+// at once, so the last hop of the layer is one small poll on every CU.
+// Then workgroup 0 publishes the next epoch once every workgroup has read
+// this call's: `arrived` holds the arrival words as read after the selection
+// (they are written at each workgroup's start, so normally all are there);
+// any that were not are polled again here.
+template <int KT>
+__device__ void moe1_combine(const Moe1Args& a, Moe1Shared& S, uint32_t epoch, uint32_t arrived) {
+  const int H = a.H, RC = H / kG1;
+  const int j0 = blockIdx.x * RC, tid = threadIdx.x;
+  const int sl = tid / RC, r = tid - sl * RC;
+  const bool in = tid < KT * RC;
+  const int e = in ? S.sidx[sl] : -1;
+  const bool mine = in && e >= 0 && e < a.E;
   const __amdgpu_buffer_rsrc_t pv = coherent_view(a.tpart, (uint32_t)((size_t)KT * H * 8));
-  for (int t0 = 0; t0 < R; t0 += kWG1) {
-    const int rl = t0 + threadIdx.x, j = b * R + rl;
-    const bool mine = rl < R && j < H;
-    float acc = 0.0f;
-    for (uint32_t it = 0;; ++it) {
-      bool missing = false;
-      acc = 0.0f;
-      if (mine) {
-        uint2 t[KT - 1];
-#pragma unroll
-        for (int sl = 0; sl < KT - 1; ++sl) t[sl] = coherent_ld_u2(pv, (uint32_t)(((size_t)sl * H + j) * 8));
-#pragma unroll
-        for (int sl = 0; sl < KT - 1; ++sl) {
-          const int ee = S.sidx[sl];
-          if (ee >= 0 && ee < a.E) {
-            missing |= t[sl].y != epoch;
-            acc += __uint_as_float(t[sl].x);
-          }
-        }
-      }
-      if (!wg_any(missing, &S.flag)) break;
-      if (it == kSpinLimit) {
-        if (threadIdx.x == 0)
-          __hip_atomic_store(&a.ctrl[kCtrlErr], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        break;
-      }
-      __builtin_amdgcn_s_sleep(2);
+  uint2 t = make_uint2(0u, 0u);
+  for (uint32_t it = 0;; ++it) {
+    t = coherent_ld_u2(pv, mine ? (uint32_t)(((size_t)sl * H + j0 + r) * 8) : 0x80000000u);
+    if (!wg_any(mine && t.y != epoch, &S.flag)) break;
+    if (it == kSpinLimit) {
+      if (tid == 0) __hip_atomic_store(&a.ctrl[kCtrlErr], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      break;
     }
-    if (mine) {
-      if (valid) acc += S.ys[rl];
-      a.out[j] = acc;
-    }
+    __builtin_amdgcn_s_sleep(2);
   }
-  // Once every workgroup has read this call's epoch (its arrival word), the
-  // next call's can be published; the words were written at the start, so
-  // the first poll normally sees them all.
-  if (b == 0) {
+  if (in) S.ys[tid] = __uint_as_float(t.x);
+  __syncthreads();
+  if (tid < RC) {
+    float acc = 0.0f;
+    for (int s2 = 0; s2 < KT; ++s2) {
+      const int e2 = S.sidx[s2];
+      if (e2 >= 0 && e2 < a.E) acc += S.ys[s2 * RC + tid];
+    }
+    a.out[j0 + tid] = acc;
+  }
+  if (blockIdx.x == 0) {
     const __amdgpu_buffer_rsrc_t av = coherent_view(&a.ctrl[kCtrlArrive], kG1 * 4);
     for (uint32_t it = 0;; ++it) {
-      const bool missing =
-          threadIdx.x < kG1 && __float_as_uint(coherent_ld(av, threadIdx.x * 4)) != epoch;
-      if (!wg_any(missing, &S.flag)) break;
+      if (it > 0 && tid < kG1) arrived = __float_as_uint(coherent_ld(av, tid * 4));
+      if (!wg_any(tid < kG1 && arrived != epoch, &S.flag)) break;
       if (it == kSpinLimit) {
-        if (threadIdx.x == 0)
-          __hip_atomic_store(&a.ctrl[kCtrlErr], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (tid == 0) __hip_atomic_store(&a.ctrl[kCtrlErr], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         break;
       }
       __builtin_amdgcn_s_sleep(2);
     }
-    if (threadIdx.x == 0)
-      __hip_atomic_store(&a.ctrl[kCtrlEpoch], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) __hip_atomic_store(&a.ctrl[kCtrlEpoch], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
-// The whole layer for one token, under a cooperative launch of kG1
-// workgroups (all resident at once).  Every workgroup has a fixed share of
-// each phase, and every expert has the same size, so the work is balanced
-// whatever the routing (the one-GPU form of slicing every expert across
-// workers, page "Kimi-K3 on the same pod, two engines", section "Reason 1"):
-//   1. router rows e = w, w + G, ...  (four at a time, a half row per wave)
+// The whole layer for one token, kG1 workgroups (all resident at once).
+// Every workgroup has a fixed share of each phase, and every expert has the
+// same size, so the work is balanced whatever the routing (the one-GPU form
+// of slicing every expert across workers, page "Kimi-K3 on the same pod, two
+// engines", section "Reason 1"):
+//   1. router: ceil(2E / G) half rows per workgroup, one per wave
 //   2. the selection: every workgroup reads all E tagged logits and runs the
 //      same top-k on them
-//   3. gate/up: slot u = w / (G/k), 32*SGU rows of I
-//   4. down: the same slot, H / (G/k) rows of H; then the workgroups of the
-//      last slot add the k slot results of their rows in slot order.
+//   3. gate/up: slot u's G/k workgroups (on one XCD), I / (G/k) rows each
+//   4. down: the same workgroups, H / (G/k) rows of H each
+//   5. combine: H / G rows per workgroup, the k slot results in slot order.
 // Hand-offs carry the call's epoch (see above); the polls form a chain
 // router -> selection -> gate/up -> down -> combine, so with every workgroup
 // resident each poll ends, and each is bounded anyway.
@@ -1355,6 +1345,10 @@ __global__ __launch_bounds__(kWG1, 1) void k_moe1(Moe1Args a) {
   __syncthreads();
   moe1_router_finish(a, S, hr, wv, epoch);
   moe1_routing(a, S, epoch, blockIdx.x == 0);
+  // the arrival words, read early (used by the combine of workgroup 0)
+  uint32_t arrived = 0u;
+  if (blockIdx.x == 0 && tid < kG1)
+    arrived = __float_as_uint(coherent_ld(coherent_view(&a.ctrl[kCtrlArrive], kG1 * 4), tid * 4));
   // Slot u's wpe workgroups: with k a multiple of kXcds they all run on one
   // XCD (workgroup w is dispatched to XCD w % kXcds), which keeps the h
   // hand-off between them in that XCD's L2.
@@ -1371,6 +1365,7 @@ __global__ __launch_bounds__(kWG1, 1) void k_moe1(Moe1Args a) {
   }
   moe1_gate_up_slice<FMT, KG, SGU>(a, S, u, b, epoch);
   moe1_down_slice<FMT, KD, SDN, KT>(a, S, u, b, a.H / wpe, epoch, xcd_local);
+  moe1_combine<KT>(a, S, epoch, arrived);
 }
 
 // ---------------------------------------------------------------------------
@@ -1602,8 +1597,8 @@ bool moe1_fits(const moe_bank* b, int C, int k) {
   if (C != 1) return false;
   const int H = b->hidden, I = b->inter;
   const bool built = (H == 7168 && I == 1536 && k == 16) || (H == 3584 && I == 3072 && (k == 16 || k == 8));
-  // the combining slice keeps its R = H / (kG1 / k) rows in LDS, one per thread
-  return built && H / (kG1 / k) <= kWG1;
+  // the combine holds k slot results of H / kG1 rows in LDS, one per thread
+  return built && H % kG1 == 0 && k * (H / kG1) <= kWG1;
 }
 
 // MOE_ERR_UNSUPPORTED when the device cannot hold all kG1 workgroups at once
