@@ -434,3 +434,104 @@ def test_prefill_k3_full_size_sampled():
     for t in sample:                    # one token at a time: 16 experts in host memory
         ref = oracle.layer(spec, Wr, x[[t]], wl.k, idx=g[[t]])
         assert_close(got[[t]], ref["out"], f"prefill token {t}")
+
+
+def test_batched_expert_fwd_invalid_and_repeated_slots():
+    """The batched path with a caller selection: slots naming experts outside
+    [0, E) contribute nothing, an expert named twice by one token counts
+    twice, and a token whose slots are all invalid gets zeros."""
+    wl = _small_prefill(5, synth.FMT_NV, "natural")
+    say("[batched] expert_fwd with invalid and repeated slots, C=5")
+    spec = wl.bank(0)
+    bank = cached_bank(spec)
+    _, x = synth.layer_inputs(wl, 0)
+    rng = np.random.default_rng(11)
+    idx = rng.integers(0, wl.E, size=(wl.C, wl.k)).astype(np.int32)
+    idx[0, 3] = -1
+    idx[1, :2] = 17                      # the same expert in two slots
+    idx[2, 5] = wl.E
+    idx[4, :] = -7                       # no valid slot at all
+    w = rng.uniform(0.05, 1.0, size=(wl.C, wl.k)).astype(np.float32)
+    out = torch.empty((wl.C, wl.H), dtype=torch.float32, device="cuda")
+    rf().moe_expert_fwd(bank, to_dev(x), wl.C, wl.k, to_dev(idx), to_dev(w), out,
+                        _ws(wl.E, wl.H, wl.I, wl.k, wl.C))
+    valid = (idx >= 0) & (idx < wl.E)
+    ref = oracle.experts_forward(spec, x, np.where(valid, idx, 0), np.where(valid, w, 0.0))
+    got = out.cpu().numpy()
+    assert np.all(got[4] == 0.0)
+    assert_close(got[:4], ref[:4], "batched expert_fwd")
+
+
+def test_decode_expert_fwd_invalid_and_repeated_slots():
+    """The one-launch decode kernel with a caller selection (W50 shape, top-16):
+    an invalid slot contributes nothing and a repeated expert counts twice."""
+    wl = synth.WORKLOADS["w50_k16"]
+    say("[decode] expert_fwd with invalid and repeated slots, W50 top-16")
+    spec = wl.bank(0)
+    bank = cached_bank(spec)
+    _, x = synth.layer_inputs(wl, 0, C=1)
+    rng = np.random.default_rng(12)
+    idx = rng.choice(wl.E, size=(1, wl.k), replace=False).astype(np.int32)
+    idx[0, 4] = -1
+    idx[0, 9] = idx[0, 2]
+    idx[0, 15] = wl.E + 3
+    w = rng.uniform(0.01, 0.2, size=(1, wl.k)).astype(np.float32)
+    out = torch.empty((1, wl.H), dtype=torch.float32, device="cuda")
+    rf().moe_expert_fwd(bank, to_dev(x), 1, wl.k, to_dev(idx), to_dev(w), out,
+                        _ws(wl.E, wl.H, wl.I, wl.k, 1))
+    valid = (idx >= 0) & (idx < wl.E)
+    ref = oracle.experts_forward(spec, x, np.where(valid, idx, 0), np.where(valid, w, 0.0))
+    assert_close(out.cpu().numpy(), ref, "decode expert_fwd")
+
+
+@pytest.mark.parametrize("E,k,C", [(64, 1, 33), (32, 32, 3)])
+def test_batched_k1_and_k_equals_E(E, k, C):
+    """Batched path at the degenerate top-k values: k = 1 (every weight is 1)
+    and k = E = 32 (every token uses every expert)."""
+    wl = _small_prefill(C, synth.FMT_MX, "natural").with_(E=E, k=k)
+    say(f"[batched] k={k} C={C}")
+    spec = wl.bank(0)
+    bank = cached_bank(spec)
+    Wr, x = synth.layer_inputs(wl, 0)
+    out = torch.empty((C, wl.H), dtype=torch.float32, device="cuda")
+    idx = torch.empty((C, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((C, k), dtype=torch.float32, device="cuda")
+    rf().moe_layer_fwd(bank, to_dev(Wr), to_dev(x), C, k, out, idx, w, _ws(wl.E, wl.H, wl.I, k, C))
+    torch.cuda.synchronize()
+    g = idx.cpu().numpy()
+    L = oracle.router_logits(x, Wr)
+    check_selection(L, g, oracle.logit_error_bound(x, Wr, route_depth(wl.H, C)), k)
+    if k == 1:
+        assert np.all(w.cpu().numpy() == 1.0)
+    else:
+        assert all(sorted(row) == list(range(wl.E)) for row in g.tolist())
+    ref = oracle.layer(spec, Wr, x, k, idx=g)
+    assert_close(out.cpu().numpy(), ref["out"], f"batched k={k}")
+
+
+def test_batched_max_tokens_sampled():
+    """The largest call the library takes (MOE_MAX_TOKENS tokens) on the small
+    batched shape with Zipf routing: the whole selection is checked against
+    the oracle's router, sampled tokens' outputs against the oracle."""
+    C = rf().MOE_MAX_TOKENS
+    wl = _small_prefill(C, synth.FMT_NV, "zipf")
+    say(f"[batched] C={C} (maximum)")
+    spec = wl.bank(0)
+    bank = cached_bank(spec)
+    Wr, x = synth.layer_inputs(wl, 0)
+    out = torch.empty((C, wl.H), dtype=torch.float32, device="cuda")
+    idx = torch.empty((C, wl.k), dtype=torch.int32, device="cuda")
+    rf().moe_layer_fwd(bank, to_dev(Wr), to_dev(x), C, wl.k, out, idx, None,
+                       _ws(wl.E, wl.H, wl.I, wl.k, C))
+    torch.cuda.synchronize()
+    g = idx.cpu().numpy()
+    L = oracle.router_logits(x, Wr)
+    check_selection(L, g, oracle.logit_error_bound(x, Wr, route_depth(wl.H, C)), wl.k)
+    counts = np.bincount(g.ravel(), minlength=wl.E)
+    hot = int(np.argmax(counts))
+    hot_tokens = np.nonzero((g == hot).any(axis=1))[0]
+    say(f"  hottest expert {hot} with {counts.max()} tokens")
+    got = out.cpu().numpy()
+    for t in sorted({0, 1, C // 2, C - 1, int(hot_tokens[0]), int(hot_tokens[-1])}):
+        ref = oracle.layer(spec, Wr, x[[t]], wl.k, idx=g[[t]])
+        assert_close(got[[t]], ref["out"], f"max-tokens token {t}")
