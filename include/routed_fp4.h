@@ -29,6 +29,13 @@
  *    be finite.  An out-of-range expert index is skipped (it contributes zero)
  *    so that a bad index never reads outside the bank.
  *  - Calls that run concurrently need separate workspaces.
+ *  - The single-launch decode kernel (one token, built shapes) hands values
+ *    between its workgroups through the workspace; every such wait is bounded.
+ *    Should one expire (other work holding CUs indefinitely), the kernel sets
+ *    the uint32 at byte offset 16 of the workspace to 1, exits, and that
+ *    call's outputs are undefined.  The word stays set until the caller
+ *    clears it (moe_workspace_init); a host can read it after the stream
+ *    has finished.
  *  - All fp32 tensors are row-major and densely packed.
  */
 #ifndef ROUTED_FP4_H
@@ -99,7 +106,7 @@ moe_status moe_bank_layout(int32_t format, int32_t hidden, int32_t inter,
 /* Limits.  Up to MOE_MAX_DECODE_TOKENS tokens per call the router is a
  * split-K mat-vec; more tokens (up to MOE_MAX_TOKENS, e.g. a prefill chunk)
  * take the batched path, whose router and expert products run on the matrix
- * cores.  The batched expert path needs H and I to be multiples of 128. */
+ * cores.  The batched expert path needs H and I to be multiples of 512. */
 #define MOE_MAX_EXPERTS 1024
 #define MOE_MAX_TOPK 32
 #define MOE_MAX_DECODE_TOKENS 16
@@ -144,11 +151,12 @@ moe_status moe_route(const float *x, const float *w_router, float *logits, int32
  * to 64 of its tokens when C > 64) for all the tokens that selected it
  * ("MUL_MAT_ID" of the "Kimi-K3 on 2x A40" page).  One token on a shape the
  * single-launch decode kernel is built for runs there; otherwise the batched
- * path runs (H, I multiples of 128), or for C <= MOE_MAX_DECODE_TOKENS and
+ * path runs (H, I multiples of 512), or for C <= MOE_MAX_DECODE_TOKENS and
  * other shapes the per-expert mat-vec kernels.
  *  x   [C][H] fp32 in; out [C][H] fp32 out (may not alias x).
- * Expert indices must be in [0, E) and distinct within a token; an index
- * outside [0, E) is skipped (its slot contributes zero). */
+ * Expert indices should be in [0, E); an index outside it is skipped (its
+ * slot contributes zero), and an expert named by several slots of a token
+ * counts once per slot. */
 moe_status moe_expert_fwd(const moe_bank *bank, const float *x, int32_t C, int32_t k,
                           const int32_t *topk_idx, const float *topk_w, float *out,
                           void *ws, size_t ws_bytes, void *stream);

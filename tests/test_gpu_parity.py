@@ -346,6 +346,8 @@ def test_layer_repeat_bit_identical(name, C):
     ix = idxs.cpu().numpy()
     assert all(np.array_equal(o[0], o[i]) for i in range(60))
     assert all(np.array_equal(ix[0], ix[i]) for i in range(60))
+    # no bounded wait of the decode kernel expired (the word at byte 16)
+    assert int(ws.tensor[4].item()) == 0
 
 
 # ---------------------------------------------------------------------------
