@@ -826,6 +826,377 @@ moe_status launch_bdma(const BArgs& a, dim3 grid, hipStream_t st) {
   return MOE_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Decode batches: each distinct expert streamed once, as dot products
+// ---------------------------------------------------------------------------
+// For C <= MOE_MAX_DECODE_TOKENS tokens the selected experts are read once
+// each (the dispatch table lists the distinct experts and their pairs), as in
+// the batch-1 kernel: 16-lane groups walk weight rows 256 contiguous bytes per
+// instruction, dequantise in registers and take dot products with the staged
+// activations of every pair of the expert.  k_dstream<GU> computes gate and up
+// (K = H) with SwiGLU into h; k_dstream<DN> computes down (K = I) times the
+// routing weight into one row per pair; k_bcombine adds each token's rows.
+//
+// Work split.  The row steps of all distinct experts (GU: 32 rows of I, one
+// gate and up row per lane group; DN: 64 rows of H, two per lane group) are
+// laid end to end and cut into one contiguous range per workgroup of equal
+// cost, a row step of expert u costing passes_u * kDCostW + tokens_u (weight
+// bytes plus per-token arithmetic).  A workgroup walks its range expert by
+// expert; for each it stages the activations of up to ntp pairs in LDS
+// (fp32, 36 floats per 32 so the 16 lanes of a group hit distinct banks) and
+// streams its rows through a register pipeline of kDPipe stages of kDSC
+// chunks per lane.
+constexpr int kDWG = 512;                  // threads per workgroup
+constexpr int kDGrp = kDWG / 16;           // 16-lane groups per workgroup
+constexpr int kDSC = 2;                    // 16-byte chunks per lane per pipeline stage
+constexpr int kDPipe = 3;                  // register buffers of the weight stream
+constexpr int kDCostW = 1;                 // cost of one weight pass of a row step, in tokens
+constexpr int kDLds = 131072;              // LDS bytes for staged activations
+constexpr int kDMaxU = MOE_MAX_DECODE_TOKENS * MOE_MAX_TOPK;   // distinct experts at most
+
+struct DArgs {
+  const uint8_t* base;
+  int64_t stride;
+  int64_t off[MOE_NUM_TENSORS];
+  int E, H, I, k, C;
+  const int32_t* disp;    // dispatch table
+  const float* x;         // [C][H]
+  const float* w;         // [C*k]
+  float* h;               // [C*k][I]
+  float* part;            // [C*k][H]
+  int ntp;                // pairs staged per pass (1, 2, 4 or 8)
+};
+
+// acc[r][t] += sum over one 32-element chunk of w_r * x_t for NR rows and the
+// first nt (<= NT) staged pairs, one 8-element dword at a time.  MXFP4: the
+// conversion applies the power-of-two scale exactly, so every product goes
+// straight into acc.  NVFP4: e2m1 values are summed per 16-element block and
+// the block's e4m3 scale multiplies the block sum.
+template <int FMT, int NR, int NT>
+__device__ __forceinline__ void chunk_dot(const uint4 (&q)[NR], const uint32_t (&sc)[NR],
+                                          const float* xs, int xoff, int ts, int nt,
+                                          float (&acc)[NR][NT]) {
+  constexpr bool MX = FMT == MOE_FMT_MXFP4;
+  float blk[NR][NT];
+  float ms[NR];
+  if (MX) {
+#pragma unroll
+    for (int r = 0; r < NR; ++r) ms[r] = __uint_as_float((sc[r] & 0xFFu) << 23);   // 2^(sc-127)
+  }
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    if (!MX && (d & 1) == 0) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        if (t >= nt) break;
+#pragma unroll
+        for (int r = 0; r < NR; ++r) blk[r][t] = 0.0f;
+      }
+    }
+    float wv[NR][8];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const uint32_t wd = (d == 0) ? q[r].x : (d == 1) ? q[r].y : (d == 2) ? q[r].z : q[r].w;
+      const float s = MX ? ms[r] : 1.0f;
+      const auto v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd, s, 0);
+      const auto v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd, s, 1);
+      const auto v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd, s, 2);
+      const auto v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd, s, 3);
+      wv[r][0] = v0[0]; wv[r][1] = v0[1]; wv[r][2] = v1[0]; wv[r][3] = v1[1];
+      wv[r][4] = v2[0]; wv[r][5] = v2[1]; wv[r][6] = v3[0]; wv[r][7] = v3[1];
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      if (t >= nt) break;
+      const float4* x4 = reinterpret_cast<const float4*>(xs + t * ts + xoff);
+      const float4 xa = x4[2 * d], xb = x4[2 * d + 1];
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        float b = MX ? acc[r][t] : blk[r][t];
+        b += wv[r][0] * xa.x; b += wv[r][1] * xa.y; b += wv[r][2] * xa.z; b += wv[r][3] * xa.w;
+        b += wv[r][4] * xb.x; b += wv[r][5] * xb.y; b += wv[r][6] * xb.z; b += wv[r][7] * xb.w;
+        if (MX) acc[r][t] = b;
+        else blk[r][t] = b;
+      }
+    }
+    if (!MX && (d & 1)) {
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        const float s = e4m3_to_f32((sc[r] >> (8 * (d >> 1))) & 0xFFu);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          if (t >= nt) break;
+          acc[r][t] += s * blk[r][t];
+        }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// One lane group's stream over `rows` rows of one expert (row ri at byte
+// offset coff[r] + ri * rstride of stream r; scales likewise), kch chunks of
+// 256 bytes per row, pipelined across rows.  done(ri, acc) gets the lane's
+// partial sums after each row's last chunk.
+template <int FMT, int NR, int NT, class Done>
+__device__ __forceinline__ void dstream_rows(const __amdgpu_buffer_rsrc_t (&crs)[NR],
+                                             const __amdgpu_buffer_rsrc_t (&srs)[NR],
+                                             const uint32_t (&coff)[NR], const uint32_t (&soff)[NR],
+                                             uint32_t rstride, uint32_t sstride, int rows, int kch,
+                                             const float* xs, int ts, int nt, Done done) {
+  const int l16 = threadIdx.x & 15;
+  constexpr int SB = (FMT == MOE_FMT_MXFP4) ? 16 : 32;   // scale bytes per chunk of a row
+  uint4 q[kDPipe][kDSC][NR];
+  uint32_t sc[kDPipe][kDSC][NR];
+  int lrow = 0, lc = 0;                  // next chunk to load
+  int crow = 0, cc = 0;                  // next chunk to multiply
+  // Loads are unconditional: past the last row the offset is out of range,
+  // which reads zeros without touching memory and keeps the count exact.
+  auto load = [&](uint4 (&qq)[kDSC][NR], uint32_t (&ss)[kDSC][NR]) {
+#pragma unroll
+    for (int b = 0; b < kDSC; ++b) {
+      const bool ok = lrow < rows;
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        const uint32_t co = ok ? coff[r] + (uint32_t)lrow * rstride + 256u * (uint32_t)lc : kNoLoad;
+        const uint32_t so = ok ? soff[r] + (uint32_t)lrow * sstride + (uint32_t)(SB * lc) : kNoLoad;
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(crs[r], (int)co, 0, kCachePolicyNt);
+        qq[b][r] = make_uint4(v[0], v[1], v[2], v[3]);
+        if (FMT == MOE_FMT_MXFP4)
+          ss[b][r] = __builtin_amdgcn_raw_buffer_load_b8(srs[r], (int)so, 0, kCachePolicyNt);
+        else
+          ss[b][r] = __builtin_amdgcn_raw_buffer_load_b16(srs[r], (int)so, 0, kCachePolicyNt);
+      }
+      if (++lc == kch) { lc = 0; ++lrow; }
+    }
+  };
+  float acc[NR][NT];
+#pragma unroll
+  for (int r = 0; r < NR; ++r)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[r][t] = 0.0f;
+  auto fma = [&](const uint4 (&qq)[kDSC][NR], const uint32_t (&ss)[kDSC][NR]) {
+#pragma unroll
+    for (int b = 0; b < kDSC; ++b) {
+      if (crow < rows) {
+        chunk_dot<FMT, NR, NT>(qq[b], ss[b], xs, (l16 + 16 * cc) * 36, ts, nt, acc);
+        if (cc == kch - 1) {
+          done(crow, acc);
+#pragma unroll
+          for (int r = 0; r < NR; ++r)
+#pragma unroll
+            for (int t = 0; t < NT; ++t) acc[r][t] = 0.0f;
+        }
+        if (++cc == kch) { cc = 0; ++crow; }
+      }
+    }
+  };
+  const int nst = (rows * kch + kDSC - 1) / kDSC;
+#pragma unroll
+  for (int j = 0; j < kDPipe - 1; ++j) load(q[j], sc[j]);
+  for (int st0 = 0; st0 < nst; st0 += kDPipe) {
+#pragma unroll
+    for (int j = 0; j < kDPipe; ++j) {
+      if (st0 + j >= nst) break;
+      __builtin_amdgcn_sched_barrier(0);
+      load(q[(j + kDPipe - 1) % kDPipe], sc[(j + kDPipe - 1) % kDPipe]);
+      __builtin_amdgcn_sched_barrier(0);
+      fma(q[j], sc[j]);
+    }
+  }
+}
+
+// Workgroup-wide exclusive scan (blockDim.x = kDWG).
+__device__ int block_excl_scan_dwg(int v, int* s_w, int* total) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int incl = wave_incl_scan(v);
+  if (lane == 63) s_w[wave] = incl;
+  __syncthreads();
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kDWG / 64; ++w) {
+    const int s = s_w[w];
+    if (w < wave) base += s;
+    tot += s;
+  }
+  __syncthreads();
+  *total = tot;
+  return base + incl - v;
+}
+
+template <int FMT, bool GU, int NT>
+__global__ __launch_bounds__(kDWG) void k_dstream(DArgs a) {
+  extern __shared__ __attribute__((aligned(16))) float xs[];   // [ntp][K / 32 * 36]
+  __shared__ int s_pref[kDMaxU + 1];
+  __shared__ int s_w[kDWG / 64];
+  __shared__ int s_bound[2];
+  __shared__ int s_pairs[MOE_MAX_DECODE_TOKENS];
+  const int tid = threadIdx.x;
+  const int CK = a.C * a.k;
+  const int nu = a.disp[0];
+  const int H = a.H, I = a.I, K = GU ? H : I, N = GU ? I : H;
+  const int B = (FMT == MOE_FMT_MXFP4) ? 32 : 16;
+  constexpr int RS = GU ? kDGrp : 2 * kDGrp;          // rows per row step
+  const int nrs = N / RS;
+  const int kch = K / 512;                            // 256-byte chunks per row
+  const int ts = K / 32 * 36;                         // LDS floats per staged pair
+  const int ntp = a.ntp;
+
+  // cost prefix over the distinct experts, then this workgroup's range
+  int ntok = 0, wu = 0;
+  if (tid < nu) {
+    ntok = a.disp[disp_untok(CK) + tid];
+    wu = ((ntok + ntp - 1) / ntp) * kDCostW + ntok;
+  }
+  int total = 0;
+  const int pre = block_excl_scan_dwg(tid < nu ? wu * nrs : 0, s_w, &total);
+  if (tid < nu) s_pref[tid] = pre;
+  if (tid == 0) {
+    s_pref[nu] = total;
+    s_bound[0] = s_bound[1] = nu * nrs;
+  }
+  __syncthreads();
+  const int G = (int)gridDim.x;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int64_t v = (int64_t)(blockIdx.x + i) * total / G;
+    if (tid < nu && v >= s_pref[tid] && v < s_pref[tid + 1]) {
+      const int rs = (int)((v - s_pref[tid] + wu - 1) / wu);   // first row step starting at or after v
+      s_bound[i] = tid * nrs + rs;
+    }
+  }
+  __syncthreads();
+  const int g0 = s_bound[0], g1 = s_bound[1];
+
+  const int grp = tid >> 4, l16 = tid & 15;
+  const uint32_t rowb = (uint32_t)(K / 2), srowb = (uint32_t)(K / B);
+  for (int u = g0 / nrs; u * nrs < g1; ++u) {
+    const int rsb = max(g0 - u * nrs, 0), rse = min(g1 - u * nrs, nrs);
+    if (rsb >= rse) continue;
+    const int e = a.disp[disp_uexp(CK) + u];
+    const int nt_u = a.disp[disp_untok(CK) + u];
+    const uint8_t* rec = a.base + (size_t)e * a.stride;
+    for (int p0 = 0; p0 < nt_u; p0 += ntp) {
+      const int nt = min(ntp, nt_u - p0);
+      __syncthreads();                                  // the previous pass is done with LDS
+      if (tid < nt) s_pairs[tid] = a.disp[disp_upair(CK) + u * a.C + p0 + tid];
+      __syncthreads();
+      for (int q = tid * 4; q < nt * K; q += kDWG * 4) {
+        const int t = q / K, kk = q - t * K;
+        const int p = s_pairs[t];
+        const float4 v = GU ? *reinterpret_cast<const float4*>(a.x + (size_t)(p / a.k) * H + kk)
+                            : *reinterpret_cast<const float4*>(a.h + (size_t)p * I + kk);
+        *reinterpret_cast<float4*>(xs + t * ts + kk + (kk >> 5) * 4) = v;
+      }
+      __syncthreads();
+      const int rows = rse - rsb;
+      if (GU) {
+        __amdgpu_buffer_rsrc_t crs[2], srs[2];
+        crs[0] = view(rec + a.off[MOE_T_GATE_CODES], (uint32_t)I * rowb);
+        crs[1] = view(rec + a.off[MOE_T_UP_CODES], (uint32_t)I * rowb);
+        srs[0] = view(rec + a.off[MOE_T_GATE_SCALES], (uint32_t)I * srowb);
+        srs[1] = view(rec + a.off[MOE_T_UP_SCALES], (uint32_t)I * srowb);
+        const int row0 = rsb * RS + grp;
+        const uint32_t coff[2] = {(uint32_t)row0 * rowb + l16 * 16, (uint32_t)row0 * rowb + l16 * 16};
+        const uint32_t soff[2] = {(uint32_t)row0 * srowb + l16 * (32 / B), (uint32_t)row0 * srowb + l16 * (32 / B)};
+        float gg = 1.0f, gu = 1.0f;
+        if (FMT == MOE_FMT_NVFP4) {
+          const float* gl = reinterpret_cast<const float*>(rec + a.off[MOE_T_GLOBALS]);
+          gg = gl[0];
+          gu = gl[1];
+        }
+        dstream_rows<FMT, 2, NT>(crs, srs, coff, soff, RS * rowb, RS * srowb, rows, kch, xs, ts, nt,
+                                 [&](int ri, float (&acc)[2][NT]) {
+          const int j = row0 + ri * RS;
+#pragma unroll
+          for (int t = 0; t < NT; ++t) {
+            if (t >= nt) break;
+            const float gs = group16_sum(acc[0][t]);
+            const float us = group16_sum(acc[1][t]);
+            if (l16 == 0) a.h[(size_t)s_pairs[t] * I + j] = silu(gg * gs) * (gu * us);
+          }
+        });
+      } else {
+        __amdgpu_buffer_rsrc_t crs[2], srs[2];
+        crs[0] = crs[1] = view(rec + a.off[MOE_T_DOWN_CODES], (uint32_t)H * rowb);
+        srs[0] = srs[1] = view(rec + a.off[MOE_T_DOWN_SCALES], (uint32_t)H * srowb);
+        const int row0 = rsb * RS + grp;                // and row0 + kDGrp
+        const uint32_t coff[2] = {(uint32_t)row0 * rowb + l16 * 16, (uint32_t)(row0 + kDGrp) * rowb + l16 * 16};
+        const uint32_t soff[2] = {(uint32_t)row0 * srowb + l16 * (32 / B),
+                                  (uint32_t)(row0 + kDGrp) * srowb + l16 * (32 / B)};
+        float gd = 1.0f;
+        if (FMT == MOE_FMT_NVFP4) gd = reinterpret_cast<const float*>(rec + a.off[MOE_T_GLOBALS])[2];
+        dstream_rows<FMT, 2, NT>(crs, srs, coff, soff, RS * rowb, RS * srowb, rows, kch, xs, ts, nt,
+                                 [&](int ri, float (&acc)[2][NT]) {
+          const int j = row0 + ri * RS;
+#pragma unroll
+          for (int t = 0; t < NT; ++t) {
+            if (t >= nt) break;
+            const int p = s_pairs[t];
+            const float wp = a.w[p] * gd;
+            const float y0 = group16_sum(acc[0][t]);
+            const float y1 = group16_sum(acc[1][t]);
+            if (l16 == 0) {
+              a.part[(size_t)p * H + j] = wp * y0;
+              a.part[(size_t)p * H + j + kDGrp] = wp * y1;
+            }
+          }
+        });
+      }
+    }
+  }
+}
+
+template <int FMT, bool GU, int NT>
+moe_status launch_dstream_nt(const DArgs& a, int grid, int lds, hipStream_t st) {
+  static bool attr_set[64] = {false};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (!attr_set[dev]) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(k_dstream<FMT, GU, NT>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kDLds) != hipSuccess)
+      return MOE_ERR_DEVICE;
+    attr_set[dev] = true;
+  }
+  hipLaunchKernelGGL((k_dstream<FMT, GU, NT>), dim3(grid), dim3(kDWG), lds, st, a);
+  return MOE_OK;
+}
+
+// The kernel instance with NT = a.ntp register slots per row for the pairs.
+template <int FMT, bool GU>
+moe_status launch_dstream(const DArgs& a, int grid, int lds, hipStream_t st) {
+  switch (a.ntp) {
+    case 1: return launch_dstream_nt<FMT, GU, 1>(a, grid, lds, st);
+    case 2: return launch_dstream_nt<FMT, GU, 2>(a, grid, lds, st);
+    case 4: return launch_dstream_nt<FMT, GU, 4>(a, grid, lds, st);
+    case 8: return launch_dstream_nt<FMT, GU, 8>(a, grid, lds, st);
+    default: return MOE_ERR_UNSUPPORTED;
+  }
+}
+
+// Pairs per activation pass: the largest of 8, 4, 2, 1 whose staged rows
+// (K / 32 * 36 floats each) fit the LDS budget; 0 if not even one does.
+int dstream_ntp(int K) {
+  const int per = K / 32 * 36 * (int)sizeof(float);
+  for (int n = 8; n >= 1; n >>= 1)
+    if (n * per <= kDLds) return n;
+  return 0;
+}
+
+// Workgroups of the decode-batch streams: one per compute unit.
+int dstream_grid() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
 moe_status status_of_launch() { return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_DEVICE; }
 
 }  // namespace
@@ -899,6 +1270,52 @@ moe_status launch_batched_experts(const moe_bank* b, const float* x, int C, int 
   else RF4_BMM(MOE_FMT_NVFP4);
 #undef RF4_BMM
   hipLaunchKernelGGL(k_bcombine, dim3((H / 4 + 255) / 256, C), dim3(256), 0, st, a);
+  return status_of_launch();
+}
+
+bool batched_decode_shape(const moe_bank* b, int C) {
+  const int H = b->hidden, I = b->inter;
+  return batched_shape_ok(b) && C >= 1 && C <= MOE_MAX_DECODE_TOKENS && dstream_ntp(H) > 0 &&
+         dstream_ntp(I) > 0 && (size_t)H * (size_t)I < ((size_t)1 << 32);
+}
+
+moe_status launch_batched_decode(const moe_bank* b, const float* x, int C, int k,
+                                 const int32_t* idx, const float* w, float* out, uint8_t* ws,
+                                 const WsLayout& L, hipStream_t st) {
+  if (!batched_decode_shape(b, C)) return MOE_ERR_UNSUPPORTED;
+  const int H = b->hidden, I = b->inter;
+  int cp = 1;                                   // C rounded up to a power of two
+  while (cp < C) cp <<= 1;
+  const int ntg = dstream_ntp(H) < cp ? dstream_ntp(H) : cp;
+  const int ntd = dstream_ntp(I) < cp ? dstream_ntp(I) : cp;
+  DArgs a;
+  a.base = static_cast<const uint8_t*>(b->base);
+  a.stride = b->expert_stride;
+  for (int t = 0; t < MOE_NUM_TENSORS; ++t) a.off[t] = b->offset[t];
+  a.E = b->num_experts; a.H = H; a.I = I; a.k = k; a.C = C;
+  a.disp = reinterpret_cast<const int32_t*>(ws + L.disp);
+  a.x = x;
+  a.w = w;
+  a.h = reinterpret_cast<float*>(ws + L.h);
+  a.part = reinterpret_cast<float*>(ws + L.part);
+  const int grid = dstream_grid();
+  moe_status m;
+  a.ntp = ntg;
+  const int lds_g = ntg * (H / 32 * 36) * (int)sizeof(float);
+  if (b->format == MOE_FMT_MXFP4) m = launch_dstream<MOE_FMT_MXFP4, true>(a, grid, lds_g, st);
+  else m = launch_dstream<MOE_FMT_NVFP4, true>(a, grid, lds_g, st);
+  if (m != MOE_OK) return m;
+  a.ntp = ntd;
+  const int lds_d = ntd * (I / 32 * 36) * (int)sizeof(float);
+  if (b->format == MOE_FMT_MXFP4) m = launch_dstream<MOE_FMT_MXFP4, false>(a, grid, lds_d, st);
+  else m = launch_dstream<MOE_FMT_NVFP4, false>(a, grid, lds_d, st);
+  if (m != MOE_OK) return m;
+  BArgs c;
+  c.E = a.E; c.H = H; c.I = I; c.k = k; c.C = C;
+  c.idx = idx;
+  c.part = a.part;
+  c.out = out;
+  hipLaunchKernelGGL(k_bcombine, dim3((H / 4 + 255) / 256, C), dim3(256), 0, st, c);
   return status_of_launch();
 }
 

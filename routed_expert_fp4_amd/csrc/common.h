@@ -319,5 +319,13 @@ moe_status launch_topk_parts(const float* lpart, int ksplit, float* logits_out, 
 moe_status launch_batched_experts(const moe_bank* b, const float* x, int C, int k,
                                   const int32_t* idx, const float* w, float* out, uint8_t* ws,
                                   const WsLayout& L, hipStream_t st);
+// launch_batched_decode: C <= MOE_MAX_DECODE_TOKENS tokens whose distinct
+// experts are listed in the workspace's dispatch table: each distinct expert
+// streamed once (gate/up with SwiGLU, then down), then the fixed-order
+// combine into out.  batched_decode_shape says which shapes it takes.
+bool batched_decode_shape(const moe_bank* b, int C);
+moe_status launch_batched_decode(const moe_bank* b, const float* x, int C, int k,
+                                 const int32_t* idx, const float* w, float* out, uint8_t* ws,
+                                 const WsLayout& L, hipStream_t st);
 
 }  // namespace rf4

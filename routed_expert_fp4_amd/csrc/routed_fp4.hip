@@ -1721,12 +1721,14 @@ moe_status moe_expert_fwd(const moe_bank* bank, const float* x, int32_t C, int32
                                      w8, L, st);
     if (m != MOE_ERR_UNSUPPORTED) return m;
   }
-  if (batched_shape(bank))
+  if (batched_shape(bank) && !batched_decode_shape(bank, C))
     return launch_batched_experts(bank, x, C, k, topk_idx, topk_w, out, w8, L, st);
   if (C > MOE_MAX_DECODE_TOKENS) return MOE_ERR_UNSUPPORTED;
   hipLaunchKernelGGL(k_dispatch, dim3(1), dim3(kWG), 0, st, topk_idx,
                      reinterpret_cast<int32_t*>(w8 + L.disp), C, k, bank->num_experts);
   if ((s = launch_status()) != MOE_OK) return s;
+  if (batched_shape(bank))
+    return launch_batched_decode(bank, x, C, k, topk_idx, topk_w, out, w8, L, st);
   return launch_experts(bank, x, C, k, topk_idx, topk_w, out, w8, L, st);
 }
 
@@ -1758,6 +1760,12 @@ moe_status moe_layer_fwd(const moe_bank* bank, const float* w_router, const floa
     s = launch_route(x, w_router, nullptr, nullptr, C, bank->hidden, bank->num_experts, k, idx, w,
                      batched ? nullptr : reinterpret_cast<int32_t*>(w8 + L.disp), w8, L, st);
   if (s != MOE_OK) return s;
+  if (batched && batched_decode_shape(bank, C)) {
+    hipLaunchKernelGGL(k_dispatch, dim3(1), dim3(kWG), 0, st, idx,
+                       reinterpret_cast<int32_t*>(w8 + L.disp), C, k, bank->num_experts);
+    if ((s = launch_status()) != MOE_OK) return s;
+    return launch_batched_decode(bank, x, C, k, idx, w, out, w8, L, st);
+  }
   if (batched) return launch_batched_experts(bank, x, C, k, idx, w, out, w8, L, st);
   return launch_experts(bank, x, C, k, idx, w, out, w8, L, st);
 }
