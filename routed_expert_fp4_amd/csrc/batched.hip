@@ -549,39 +549,85 @@ __global__ __launch_bounds__(256) void k_brouter(const float* x, const float* Wr
 // weights.  The logits are given, or are the sums of ksplit partial sums
 // lpart[s][t][e], added in split order (and then stored to logits_out if
 // that is not null).
-__global__ __launch_bounds__(512) void k_btopk(const float* logits, const float* lpart, int ksplit,
-                                               float* logits_out, int C, int E, int k, int32_t* idx,
-                                               float* w) {
-  __shared__ SelectLds S[8];
+// One wave per token.  With `disp`, all C <= 16 tokens are in this one
+// workgroup (1024 threads) and it also writes the dispatch table: distinct
+// experts in order of first use (pair order), each with its pairs in token
+// order.  A router selection names distinct experts per token, so the pairs
+// of expert e are marked by a token bitmask and a pair's place in the list is
+// the number of earlier tokens in the mask.
+template <int NW>
+__global__ __launch_bounds__(64 * NW) void k_btopk(const float* logits, const float* lpart, int ksplit,
+                                                   float* logits_out, int C, int E, int k,
+                                                   int32_t* idx, float* w, int32_t* disp) {
+  __shared__ SelectLds S[NW];
   constexpr int NPL = MOE_MAX_EXPERTS / 64;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 8 + wave;
-  if (t >= C) return;                       // whole waves leave; no barrier follows
-  uint64_t ck[NPL];
-  float lv[NPL];
+  const int t = blockIdx.x * NW + wave;
+  if (t < C) {
+    uint64_t ck[NPL];
+    float lv[NPL];
+    if (lpart) {
+      // every partial load in flight before the first add; added in split order
+      float pv[kKsplitMax][NPL];
 #pragma unroll
-  for (int i = 0; i < NPL; ++i) {
-    const int e = lane + 64 * i;
-    float l = 0.0f;
-    if (e < E) {
-      if (lpart) {
-        l = lpart[(size_t)t * E + e];
-        for (int s = 1; s < ksplit; ++s) l += lpart[((size_t)s * C + t) * E + e];
-        if (logits_out) logits_out[(size_t)t * E + e] = l;
-      } else {
-        l = logits[(size_t)t * E + e];
+      for (int sp = 0; sp < kKsplitMax; ++sp)
+#pragma unroll
+        for (int i = 0; i < NPL; ++i) {
+          const int e = lane + 64 * i;
+          pv[sp][i] = (e < E && sp < ksplit) ? lpart[((size_t)sp * C + t) * E + e] : 0.0f;
+        }
+#pragma unroll
+      for (int i = 0; i < NPL; ++i) {
+        float l = pv[0][i];
+#pragma unroll
+        for (int sp = 1; sp < kKsplitMax; ++sp)
+          if (sp < ksplit) l += pv[sp][i];
+        lv[i] = l;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NPL; ++i) {
+        const int e = lane + 64 * i;
+        lv[i] = e < E ? logits[(size_t)t * E + e] : 0.0f;
       }
     }
-    lv[i] = l;
-    ck[i] = e < E ? sel_key(lv[i], e) : 0;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+      const int e = lane + 64 * i;
+      if (lpart && logits_out && e < E) logits_out[(size_t)t * E + e] = lv[i];
+      ck[i] = e < E ? sel_key(lv[i], e) : 0;
+    }
+    wave_select<NPL>(ck, lv, k, S[wave]);
+    const float l = lane < k ? S[wave].sel_l[lane] : 0.0f;
+    const float wt = route_weight(l, lane, k);
+    if (lane < k) {
+      idx[(size_t)t * k + lane] = S[wave].sel_e[lane];
+      w[(size_t)t * k + lane] = wt;
+    }
   }
-  wave_select<NPL>(ck, lv, k, S[wave]);
-  const float l = lane < k ? S[wave].sel_l[lane] : 0.0f;
-  const float wt = route_weight(l, lane, k);
-  if (lane < k) {
-    idx[(size_t)t * k + lane] = S[wave].sel_e[lane];
-    w[(size_t)t * k + lane] = wt;
+  if (NW < MOE_MAX_DECODE_TOKENS || !disp) return;   // uniform: no barrier follows
+  __shared__ uint32_t s_mask[MOE_MAX_EXPERTS];
+  __shared__ int s_uof[MOE_MAX_EXPERTS];
+  __shared__ int s_w[48];
+  const int tid = threadIdx.x, CK = C * k;
+  for (int e = tid; e < E; e += 64 * NW) s_mask[e] = 0u;
+  __syncthreads();
+  const int pt = tid / k, ps = tid - pt * k;          // pair tid = (token, slot)
+  const int pe = tid < CK ? S[pt].sel_e[ps] : -1;
+  if (tid < CK) atomicOr(&s_mask[pe], 1u << pt);
+  __syncthreads();
+  const uint32_t m = tid < CK ? s_mask[pe] : 0u;
+  const int first = (tid < CK && (int)__builtin_ctz(m) == pt) ? 1 : 0;
+  int nu = 0;
+  const int u = block_excl_scan_1024(first, s_w, &nu);
+  if (first) {
+    s_uof[pe] = u;
+    disp[disp_uexp(CK) + u] = pe;
+    disp[disp_untok(CK) + u] = __builtin_popcount(m);
   }
+  __syncthreads();
+  if (tid < CK) disp[disp_upair(CK) + s_uof[pe] * C + __builtin_popcount(m & ((1u << pt) - 1u))] = tid;
+  if (tid == 0) disp[0] = nu;
 }
 
 // ---------------------------------------------------------------------------
@@ -1043,11 +1089,8 @@ __global__ __launch_bounds__(kDWG) void k_dstream(DArgs a) {
   const int ntp = a.ntp;
 
   // cost prefix over the distinct experts, then this workgroup's range
-  int ntok = 0, wu = 0;
-  if (tid < nu) {
-    ntok = a.disp[disp_untok(CK) + tid];
-    wu = ((ntok + ntp - 1) / ntp) * kDCostW + ntok;
-  }
+  const int ntok = tid < CK ? a.disp[disp_untok(CK) + tid] : 0;   // loaded beside nu
+  const int wu = tid < nu ? ((ntok + ntp - 1) / ntp) * kDCostW + ntok : 0;
   int total = 0;
   const int pre = block_excl_scan_dwg(tid < nu ? wu * nrs : 0, s_w, &total);
   if (tid < nu) s_pref[tid] = pre;
@@ -1212,15 +1255,21 @@ moe_status launch_batched_route(const float* x, const float* Wr, const float* lo
                        C, H, E);
     lg = dst;
   }
-  hipLaunchKernelGGL(k_btopk, dim3((C + 7) / 8), dim3(512), 0, st, lg, nullptr, 0, nullptr, C, E, k,
-                     idx, w);
+  hipLaunchKernelGGL(k_btopk<8>, dim3((C + 7) / 8), dim3(512), 0, st, lg, nullptr, 0, nullptr, C, E,
+                     k, idx, w, nullptr);
   return status_of_launch();
 }
 
 moe_status launch_topk_parts(const float* lpart, int ksplit, float* logits_out, int C, int E, int k,
-                             int32_t* idx, float* w, hipStream_t st) {
-  hipLaunchKernelGGL(k_btopk, dim3((C + 7) / 8), dim3(512), 0, st, nullptr, lpart, ksplit,
-                     logits_out, C, E, k, idx, w);
+                             int32_t* idx, float* w, int32_t* disp, hipStream_t st) {
+  if (disp) {
+    if (C > MOE_MAX_DECODE_TOKENS || C * k > 1024) return MOE_ERR_UNSUPPORTED;
+    hipLaunchKernelGGL(k_btopk<MOE_MAX_DECODE_TOKENS>, dim3(1), dim3(64 * MOE_MAX_DECODE_TOKENS), 0,
+                       st, nullptr, lpart, ksplit, logits_out, C, E, k, idx, w, disp);
+  } else {
+    hipLaunchKernelGGL(k_btopk<8>, dim3((C + 7) / 8), dim3(512), 0, st, nullptr, lpart, ksplit,
+                       logits_out, C, E, k, idx, w, nullptr);
+  }
   return status_of_launch();
 }
 

@@ -311,9 +311,10 @@ moe_status launch_batched_route(const float* x, const float* Wr, const float* lo
                                 float* w, uint8_t* ws, const WsLayout& L, hipStream_t st);
 // launch_topk_parts: the top-k of C tokens (one wave each) from ksplit
 // partial router sums lpart[s][t][e], added in split order; the logits go to
-// logits_out too when it is not null.
+// logits_out too when it is not null, and the dispatch table to disp when it
+// is not null (C <= MOE_MAX_DECODE_TOKENS).
 moe_status launch_topk_parts(const float* lpart, int ksplit, float* logits_out, int C, int E, int k,
-                             int32_t* idx, float* w, hipStream_t st);
+                             int32_t* idx, float* w, int32_t* disp, hipStream_t st);
 // launch_batched_experts: the selected experts of C tokens as grouped GEMMs
 // on the matrix cores, then the fixed-order combine into out.
 moe_status launch_batched_experts(const moe_bank* b, const float* x, int C, int k,

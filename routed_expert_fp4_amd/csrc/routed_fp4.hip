@@ -1498,14 +1498,16 @@ moe_status launch_route(const float* x, const float* Wr, const float* logits_in,
     a.ksplit = 1;
     a.kper = H;
   }
-  // Several tokens and no dispatch table: the top-k runs as its own launch,
-  // one wave per token, instead of token after token in the last workgroup.
-  a.select = (x && C > 1 && !disp) ? 0 : 1;
+  // Several tokens: the top-k (and the dispatch table) runs as its own
+  // launch, one wave per token, instead of token after token in the last
+  // workgroup.
+  a.select = (x && C > 1) ? 0 : 1;
   if (C == 1) hipLaunchKernelGGL(k_route<1>, dim3(grid), dim3(kWG), 0, st, a);
   else if (C <= 4) hipLaunchKernelGGL(k_route<4>, dim3(grid), dim3(kWG), 0, st, a);
   else hipLaunchKernelGGL(k_route<16>, dim3(grid), dim3(kWG), 0, st, a);
   moe_status s = launch_status();
-  if (s == MOE_OK && !a.select) s = launch_topk_parts(a.lpart, a.ksplit, logits_out, C, E, k, idx, w, st);
+  if (s == MOE_OK && !a.select)
+    s = launch_topk_parts(a.lpart, a.ksplit, logits_out, C, E, k, idx, w, disp, st);
   return s;
 }
 
@@ -1758,14 +1760,13 @@ moe_status moe_layer_fwd(const moe_bank* bank, const float* w_router, const floa
                              idx, w, w8, L, st);
   else
     s = launch_route(x, w_router, nullptr, nullptr, C, bank->hidden, bank->num_experts, k, idx, w,
-                     batched ? nullptr : reinterpret_cast<int32_t*>(w8 + L.disp), w8, L, st);
+                     (batched && !batched_decode_shape(bank, C))
+                         ? nullptr
+                         : reinterpret_cast<int32_t*>(w8 + L.disp),
+                     w8, L, st);
   if (s != MOE_OK) return s;
-  if (batched && batched_decode_shape(bank, C)) {
-    hipLaunchKernelGGL(k_dispatch, dim3(1), dim3(kWG), 0, st, idx,
-                       reinterpret_cast<int32_t*>(w8 + L.disp), C, k, bank->num_experts);
-    if ((s = launch_status()) != MOE_OK) return s;
+  if (batched && batched_decode_shape(bank, C))
     return launch_batched_decode(bank, x, C, k, idx, w, out, w8, L, st);
-  }
   if (batched) return launch_batched_experts(bank, x, C, k, idx, w, out, w8, L, st);
   return launch_experts(bank, x, C, k, idx, w, out, w8, L, st);
 }
