@@ -276,8 +276,13 @@ def main():
     fmt = "nvfp4" if wl.fmt == synth.FMT_NV else "mxfp4"
     if C == 1 and wl.name != "tiny":
         kernel = "k_moe1 (whole layer, one launch per moe_layer_fwd call)"
+    elif wl.name == "tiny":
+        kernel = "k_route + k_btopk + k_gate_up + k_down (+ k_zero_uncovered) per moe_layer_fwd call"
+    elif C <= 16:
+        kernel = "k_route + k_btopk + k_dstream<GU> + k_dstream<DN> + k_bcombine per moe_layer_fwd call"
     else:
-        kernel = "k_route + k_gate_up + k_down (+ k_zero_uncovered) per moe_layer_fwd call"
+        kernel = ("k_brouter + k_btopk + k_bsplit/k_bcount/k_bscan/k_bscatter + k_bdma or k_bmm "
+                  "(gate/up, down) + k_bcombine per moe_layer_fwd call")
 
     result = {
         "metric": METRIC,

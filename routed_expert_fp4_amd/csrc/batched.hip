@@ -1,7 +1,8 @@
-// libroutedfp4, batched path: the routed experts of many tokens at once as
-// grouped GEMMs on the CDNA4 matrix cores.
+// libroutedfp4, batched path: the routed experts of many tokens at once,
+// as row dot products for decode batches (C = 2..16) and as grouped GEMMs on
+// the CDNA4 matrix cores for wider calls (prefill chunks).
 //
-// Used for C >= 2 tokens per call (decode batches and prefill chunks).  The
+// Used for C >= 2 tokens per call.  The
 // layer is the same as the decode path's (page "Kimi-K3 on 2x A40 -- measured
 // findings", section "Why the placement experiments all looked the same":
 // MUL_MAT_ID over the selected experts; page "SparkInfer-K3", section "How the
@@ -20,7 +21,13 @@
 // down product as two pieces (hi + lo), which carry h to within 2^-17
 // relative.  The NVFP4 per-tensor scale multiplies the accumulated sums.
 //
-// Kernels, in stream order:
+// Decode batches (C <= 16), in stream order (precision as the batch-1
+// kernel: fp32 products and sums):
+//   k_btopk<16> the top-k of every token, then the dispatch table
+//   k_dstream   gate/up with SwiGLU, then down: each distinct expert streamed
+//               once over cost-balanced row ranges (see "Decode batches")
+//   k_bcombine  out[t] = sum of its pairs' rows in slot order
+// Wider calls, in stream order:
 //   k_bsplit    x -> three bf16 planes + per-token flags (zeroes the counters)
 //   k_bcount    (token, slot) pairs per expert
 //   k_bscan     offsets and the tile list (each expert's pairs in tiles of
