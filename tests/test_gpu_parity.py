@@ -537,3 +537,63 @@ def test_batched_max_tokens_sampled():
     for t in sorted({0, 1, C // 2, C - 1, int(hot_tokens[0]), int(hot_tokens[-1])}):
         ref = oracle.layer(spec, Wr, x[[t]], wl.k, idx=g[[t]])
         assert_close(got[[t]], ref["out"], f"max-tokens token {t}")
+
+
+# ---------------------------------------------------------------------------
+# Decode batches (C = 2..16): each distinct expert streamed once
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("C,k,fmt", [(16, 8, synth.FMT_NV), (16, 32, synth.FMT_MX), (9, 4, synth.FMT_MX)])
+def test_decode_batch_passes_and_limits(C, k, fmt):
+    """64 experts, H 1024, I 512, fp32 tokens with Zipf routing: experts chosen
+    by more tokens than one activation pass holds (8) take several passes over
+    their weights; C = 16 with k = 32 is the largest pair count (512)."""
+    wl = synth.Workload(f"dsmall_{C}_{k}", fmt, 64, k, 1024, 512, C, 1, "zipf", 1.0, False)
+    say(f"[decode batch] C={C} k={k} fmt={fmt}")
+    spec = wl.bank(0)
+    bank = cached_bank(spec)
+    Wr, x = synth.layer_inputs(wl, 0)
+    out = torch.empty((C, wl.H), dtype=torch.float32, device="cuda")
+    idx = torch.empty((C, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((C, k), dtype=torch.float32, device="cuda")
+    rf().moe_layer_fwd(bank, to_dev(Wr), to_dev(x), C, k, out, idx, w, _ws(wl.E, wl.H, wl.I, k, C))
+    torch.cuda.synchronize()
+    g = idx.cpu().numpy()
+    L = oracle.router_logits(x, Wr)
+    check_selection(L, g, oracle.logit_error_bound(x, Wr, route_depth(wl.H, C)), k)
+    counts = np.bincount(g.ravel(), minlength=wl.E)
+    say(f"  most tokens on one expert: {counts.max()}; distinct experts: {np.count_nonzero(counts)}")
+    if C == 16:
+        assert counts.max() > 8                   # the multi-pass case is exercised
+    wref = np.stack([oracle.route_weights(L[t, g[t]]) for t in range(C)])
+    np.testing.assert_allclose(w.cpu().numpy(), wref, rtol=1e-5)
+    ref = oracle.layer(spec, Wr, x, k, idx=g)
+    assert_close(out.cpu().numpy(), ref["out"], f"decode batch C={C} k={k}")
+
+
+def test_decode_batch_k3_shape_sampled():
+    """The K3 shape (H 7168: four pairs per gate/up activation pass) with 12
+    tokens and Zipf 1.2 routing; sampled tokens, among them two of the most
+    loaded expert, against the oracle."""
+    wl = synth.WORKLOADS["k3_stack_zipf"]
+    C = 12
+    say(f"[decode batch] K3 shape C={C}")
+    spec = wl.bank(0)
+    bank = cached_bank(spec)
+    Wr, x = synth.layer_inputs(wl, 0, C=C)
+    out = torch.empty((C, wl.H), dtype=torch.float32, device="cuda")
+    idx = torch.empty((C, wl.k), dtype=torch.int32, device="cuda")
+    rf().moe_layer_fwd(bank, to_dev(Wr), to_dev(x), C, wl.k, out, idx, None,
+                       _ws(wl.E, wl.H, wl.I, wl.k, C))
+    torch.cuda.synchronize()
+    g = idx.cpu().numpy()
+    L = oracle.router_logits(x, Wr)
+    check_selection(L, g, oracle.logit_error_bound(x, Wr, route_depth(wl.H, C)), wl.k)
+    counts = np.bincount(g.ravel(), minlength=wl.E)
+    hot = int(np.argmax(counts))
+    say(f"  hottest expert {hot} with {counts.max()} tokens")
+    assert counts.max() > 4                       # more than one gate/up pass
+    hot_tokens = np.nonzero((g == hot).any(axis=1))[0]
+    got = out.cpu().numpy()
+    for t in sorted({0, int(hot_tokens[0]), int(hot_tokens[-1])}):
+        ref = oracle.layer(spec, Wr, x[[t]], wl.k, idx=g[[t]])
+        assert_close(got[[t]], ref["out"], f"K3 decode batch token {t}")
