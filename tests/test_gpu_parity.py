@@ -542,11 +542,14 @@ def test_batched_max_tokens_sampled():
 # ---------------------------------------------------------------------------
 # Decode batches (C = 2..16): each distinct expert streamed once
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("C,k,fmt", [(16, 8, synth.FMT_NV), (16, 32, synth.FMT_MX), (9, 4, synth.FMT_MX)])
+@pytest.mark.parametrize("C,k,fmt", [(16, 8, synth.FMT_NV), (16, 32, synth.FMT_MX), (9, 4, synth.FMT_MX),
+                                     (1, 8, synth.FMT_NV), (2, 1, synth.FMT_MX)])
 def test_decode_batch_passes_and_limits(C, k, fmt):
     """64 experts, H 1024, I 512, fp32 tokens with Zipf routing: experts chosen
     by more tokens than one activation pass holds (8) take several passes over
-    their weights; C = 16 with k = 32 is the largest pair count (512)."""
+    their weights; C = 16 with k = 32 is the largest pair count (512); C = 1
+    (a shape the one-launch kernel is not built for) selects in the router's
+    last workgroup; k = 1."""
     wl = synth.Workload(f"dsmall_{C}_{k}", fmt, 64, k, 1024, 512, C, 1, "zipf", 1.0, False)
     say(f"[decode batch] C={C} k={k} fmt={fmt}")
     spec = wl.bank(0)
