@@ -46,6 +46,9 @@ def parse():
                             "w50_c7_k16", "tiny", "k3_prefill"],
                    help="k3_stack (the headline: 12 layers, uniform routing), k3_stack_zipf "
                         "(Zipf s=1.2), or one of the single-layer decode workloads")
+    p.add_argument("--tokens", type=int, default=0,
+                   help="tokens per call instead of the workload's own (a sweep over C reuses "
+                        "one workload's bank, routing and shapes)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-layers", type=int, default=1,
                    help="layer-tokens of the workload the CPU oracle is timed on")
@@ -175,6 +178,8 @@ def main():
         sd.build()
 
     wl = synth.WORKLOADS[args.workload]
+    if args.tokens > 0:
+        wl = wl.with_(C=args.tokens)
     pool = POOL if wl.C <= 16 else 2
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
