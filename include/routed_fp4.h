@@ -104,9 +104,11 @@ moe_status moe_bank_layout(int32_t format, int32_t hidden, int32_t inter,
                            int64_t offset[MOE_NUM_TENSORS], int64_t *expert_stride);
 
 /* Limits.  Up to MOE_MAX_DECODE_TOKENS tokens per call the router is a
- * split-K mat-vec; more tokens (up to MOE_MAX_TOKENS, e.g. a prefill chunk)
- * take the batched path, whose router and expert products run on the matrix
- * cores.  The batched expert path needs H and I to be multiples of 512. */
+ * split-K mat-vec and the experts run as row dot products (each distinct
+ * expert streamed once for all its tokens); more tokens (up to
+ * MOE_MAX_TOKENS, e.g. a prefill chunk) take the batched path, whose router
+ * and expert products run on the matrix cores.  Both batched expert paths
+ * need H and I to be multiples of 512. */
 #define MOE_MAX_EXPERTS 1024
 #define MOE_MAX_TOPK 32
 #define MOE_MAX_DECODE_TOKENS 16
@@ -150,9 +152,11 @@ moe_status moe_route(const float *x, const float *w_router, float *logits, int32
  * Each distinct expert's weights are read once per call (once per tile of up
  * to 64 of its tokens when C > 64) for all the tokens that selected it
  * ("MUL_MAT_ID" of the "Kimi-K3 on 2x A40" page).  One token on a shape the
- * single-launch decode kernel is built for runs there; otherwise the batched
- * path runs (H, I multiples of 512), or for C <= MOE_MAX_DECODE_TOKENS and
- * other shapes the per-expert mat-vec kernels.
+ * single-launch decode kernel is built for runs there; otherwise, for H and I
+ * multiples of 512, C <= MOE_MAX_DECODE_TOKENS runs the decode-batch row
+ * streams and larger C the matrix-core grouped GEMMs; for
+ * C <= MOE_MAX_DECODE_TOKENS and other shapes the per-expert mat-vec kernels
+ * run.
  *  x   [C][H] fp32 in; out [C][H] fp32 out (may not alias x).
  * Expert indices should be in [0, E); an index outside it is skipped (its
  * slot contributes zero), and an expert named by several slots of a token
