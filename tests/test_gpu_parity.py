@@ -600,3 +600,25 @@ def test_decode_batch_k3_shape_sampled():
     for t in sorted({0, int(hot_tokens[0]), int(hot_tokens[-1])}):
         ref = oracle.layer(spec, Wr, x[[t]], wl.k, idx=g[[t]])
         assert_close(got[[t]], ref["out"], f"K3 decode batch token {t}")
+
+
+@pytest.mark.parametrize("E,k,H,I,C,fmt", [(16, 4, 512, 512, 6, synth.FMT_NV), (1024, 32, 512, 1024, 16, synth.FMT_MX)])
+def test_decode_batch_shape_limits(E, k, H, I, C, fmt):
+    """The smallest rows the decode-batch streams take (one 256-byte chunk per
+    row at H = 512) and the largest distinct-expert count (1024 experts,
+    top-32, 16 tokens: up to 512 distinct experts)."""
+    wl = synth.Workload(f"dlim_{E}_{k}_{H}", fmt, E, k, H, I, C, 1, "natural", 0.0, False)
+    say(f"[decode batch] E={E} k={k} H={H} I={I} C={C}")
+    spec = wl.bank(0)
+    bank = cached_bank(spec)
+    Wr, x = synth.layer_inputs(wl, 0)
+    out = torch.empty((C, H), dtype=torch.float32, device="cuda")
+    idx = torch.empty((C, k), dtype=torch.int32, device="cuda")
+    rf().moe_layer_fwd(bank, to_dev(Wr), to_dev(x), C, k, out, idx, None, _ws(E, H, I, k, C))
+    torch.cuda.synchronize()
+    g = idx.cpu().numpy()
+    L = oracle.router_logits(x, Wr)
+    check_selection(L, g, oracle.logit_error_bound(x, Wr, route_depth(H, C)), k)
+    say(f"  distinct experts: {len(np.unique(g))}")
+    ref = oracle.layer(spec, Wr, x, k, idx=g)
+    assert_close(out.cpu().numpy(), ref["out"], f"decode batch E={E} k={k} H={H}")
