@@ -43,9 +43,11 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="k3_stack",
                    choices=["k3_stack", "k3_stack_zipf", "w50_k16", "w50_k8", "w50_c7_k8",
-                            "w50_c7_k16", "tiny", "k3_prefill"],
+                            "w50_c7_k16", "tiny", "k3_prefill", "k3_latent"],
                    help="k3_stack (the headline: 12 layers, uniform routing), k3_stack_zipf "
-                        "(Zipf s=1.2), or one of the single-layer decode workloads")
+                        "(Zipf s=1.2), one of the single-layer decode workloads, or k3_latent "
+                        "(whole latent layers: router, routed_down, routed experts, norm, "
+                        "routed_up, shared experts)")
     p.add_argument("--tokens", type=int, default=0,
                    help="tokens per call instead of the workload's own (a sweep over C reuses "
                         "one workload's bank, routing and shapes)")
@@ -155,6 +157,137 @@ def cpu_baseline(wl, layers: int, max_tokens: int = 8):
             "kind": "oracle", "sample": sample}
 
 
+def cpu_baseline_latent(wl):
+    """The oracle as it is on one token of the latent workload's first layer:
+    router, routed_down, dequantisation and FFN of each selected routed expert,
+    the combine, the norm, routed_up and the shared experts; bank byte
+    regeneration (synth) is done before the timing."""
+    import numpy as np
+    import oracle
+    import synth
+    oracle.build()
+    Wr, x, Wd, Wu, g = synth.latent_inputs(wl, 0, pool=0, C=1)
+    _, idx, _ = oracle.route(x, Wr, wl.k)
+    rs, ss = wl.routed_bank(0), wl.shared_bank(0)
+    rt = {int(e): synth.expert_tensors(rs, int(e)) for e in np.unique(idx)}
+    st = {j: synth.expert_tensors(ss, j) for j in range(wl.n_shared)}
+
+    def deq(spec, t):
+        gl = t["globals"]
+        return (oracle.dequant(spec.fmt, t["gate_codes"], t["gate_scales"], gl[0]),
+                oracle.dequant(spec.fmt, t["up_codes"], t["up_scales"], gl[1]),
+                oracle.dequant(spec.fmt, t["down_codes"], t["down_scales"], gl[2]))
+
+    t0 = time.perf_counter()
+    rc = {e: deq(rs, t) for e, t in rt.items()}
+    sc = {j: deq(ss, t) for j, t in st.items()}
+    oracle.latent_layer(wl, Wr, x, Wd, Wu, g, routed_cache=rc, shared_cache=sc)
+    us = (time.perf_counter() - t0) * 1e6
+    return {"value": us, "unit": "us/token per latent MoE layer",
+            "cores": int(oracle.lib().orc_threads()), "kind": "oracle",
+            "sample": "1 token of layer 0 (pool draw 0): dequantisation of the selected routed "
+                      "experts and the shared experts, router, routed_down, expert FFNs, combine, "
+                      "norm, routed_up, shared FFNs; bank byte regeneration not timed"}
+
+
+def bench_latent(args, wl):
+    """Latent MoE layers (router on x, routed_down, routed experts in the
+    latent width, RMS norm of their sum, routed_up, shared experts), one
+    moe_latent_layer_fwd call per layer per step."""
+    import numpy as np
+    import torch
+    import routed_expert_fp4_amd as rf
+    import synth
+    import synth.device as sd
+
+    if args.tokens > 0:
+        wl = wl.with_(C=args.tokens)
+    C, pool = wl.C, POOL
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    t_setup = time.perf_counter()
+    layers, xs, keep = [], [], []
+    for l in range(wl.layers):
+        rs, ss = wl.routed_bank(l), wl.shared_bank(l)
+        rb = rf.Bank(wl.fmt, wl.E, wl.L, wl.I, device=dev)
+        sb = rf.Bank(wl.fmt, wl.n_shared, wl.H, wl.I_shared, device=dev)
+        sd.fill_bank(rb.storage.data_ptr(), rb.offsets, rb.stride, rs, stream.cuda_stream)
+        sd.fill_bank(sb.storage.data_ptr(), sb.offsets, sb.stride, ss, stream.cuda_stream)
+        Wr, x, Wd, Wu, g = synth.latent_inputs(wl, l, pool=0, C=pool * C)
+        t = [torch.from_numpy(Wr).to(dev), torch.from_numpy(Wd.view(np.int16)).to(dev),
+             torch.from_numpy(g).to(dev), torch.from_numpy(Wu.view(np.int16)).to(dev)]
+        layers.append(rf.LatentLayer(t[0], t[1], t[2], wl.eps, t[3], rb, sb))
+        xs.append(torch.from_numpy(x).to(dev))
+        keep.append((rb, sb, t))
+    torch.cuda.synchronize()
+    log(f"setup {time.perf_counter() - t_setup:.1f}s: {wl.layers} latent layers")
+    ws = rf.LatentWorkspace(layers[0], wl.k, C, device=dev)
+    outs = [torch.empty((C, wl.H), dtype=torch.float32, device=dev) for _ in range(wl.layers)]
+    idx = [[torch.empty((C, wl.k), dtype=torch.int32, device=dev) for _ in range(pool)]
+           for _ in range(wl.layers)]
+
+    def step(i):
+        j = i % pool
+        for l in range(wl.layers):
+            rf.moe_latent_layer_fwd(layers[l], xs[l][j * C:(j + 1) * C], C, wl.k, outs[l],
+                                    idx[l][j], None, ws)
+
+    for i in range(max(args.warmup, pool)):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = e0.elapsed_time(e1) / args.steps
+    us_call = ms_step * 1000.0 / wl.layers
+    uniq = np.mean([len(np.unique(idx[l][j].cpu().numpy())) for l in range(wl.layers)
+                    for j in range(pool)])
+    rexp, sexp = wl.routed_bank(0).expert_bytes(), wl.shared_bank(0).expert_bytes()
+    dense_bytes = wl.E * wl.H * 4 + 2 * wl.L * wl.H * 2 + wl.L * 4
+    alg_bytes = uniq * rexp + wl.n_shared * sexp + dense_bytes + 2 * C * wl.H * 4
+    gbps = alg_bytes / (us_call * 1e-6) / 1e9
+    fmt = "nvfp4" if wl.fmt == synth.FMT_NV else "mxfp4"
+    routed_kernel = "k_moe1 (routed experts, selection given)" if C == 1 else \
+        "k_dispatch + k_dstream<GU> + k_dstream<DN> + k_bcombine (routed experts)"
+    result = {
+        "metric": "latent MoE layer decode µs/token + achieved HBM GB/s (% of peak)",
+        "value": round(us_call / C, 3),
+        "unit": "us/token per latent MoE layer",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": f"synthetic (seeded {fmt} banks generated on device, bf16 N(0,1/K) dense "
+                "matrices, fp32 N(0,1) tokens, N(0,0.02) router)",
+        "config": {"workload": f"{wl.name}: {wl.layers} latent MoE layer(s): router on H {wl.H}, "
+                               f"routed_down {wl.H}->{wl.L}, {wl.E} routed experts top-{wl.k} "
+                               f"(H {wl.L}, I {wl.I}), norm, routed_up {wl.L}->{wl.H}, "
+                               f"{wl.n_shared} shared experts (H {wl.H}, I {wl.I_shared}), {fmt}, "
+                               f"{C} token(s) per call",
+                   "layers": wl.layers, "experts": wl.E, "top_k": wl.k, "hidden": wl.H,
+                   "latent": wl.L, "inter": wl.I, "shared": wl.n_shared, "format": fmt,
+                   "tokens_per_call": C},
+        "us_per_call": round(us_call, 3),
+        "tokens_per_s": round(1000.0 * C / ms_step, 2),
+        "distinct_experts_per_call": round(float(uniq), 2),
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "k_route + k_btopk (router), k_gemv (routed_down), " + routed_kernel
+                               + ", k_shared_sel + shared experts, k_gemv (norm + routed_up) "
+                               "per moe_latent_layer_fwd call",
+                     "bytes_per_launch": int(alg_bytes), "us_per_launch": round(us_call, 3)},
+        "wall_s_timed": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle ...")
+        result["cpu_baseline"] = cpu_baseline_latent(wl)
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -177,6 +310,10 @@ def main():
     if not os.path.exists(sd.LIB):
         sd.build()
 
+    if args.workload in synth.LATENT_WORKLOADS:
+        torch.cuda.set_device(0)
+        bench_latent(args, synth.LATENT_WORKLOADS[args.workload])
+        return
     wl = synth.WORKLOADS[args.workload]
     if args.tokens > 0:
         wl = wl.with_(C=args.tokens)

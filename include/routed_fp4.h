@@ -172,6 +172,48 @@ moe_status moe_layer_fwd(const moe_bank *bank, const float *w_router, const floa
                          int32_t C, int32_t k, float *out, int32_t *topk_idx_out,
                          float *topk_w_out, void *ws, size_t ws_bytes, void *stream);
 
+/* A latent MoE layer: the steps either side of the routed experts (page
+ * "SparkInfer-K3", section "How the TP module works": router -> routed_down ->
+ * routed experts, then routed_norm -> routed_up -> shared experts; section
+ * "Why the reduce is at 3584 and not 7168": the RMS norm comes after the sum
+ * of the routed experts; section "The model": 896 routed experts, top-16, 2
+ * shared experts, latent width 3584, expert FFN 3072).
+ *   idx, w  = top-k of x W_r^T, as moe_route            (router on the hidden x)
+ *   x_lat   = W_down x                                   ([L][H] bf16)
+ *   y_lat   = sum_s w_s FFN_e(s)(x_lat)                  (routed bank, hidden = L)
+ *   out     = W_up (gamma * y_lat / sqrt(mean(y_lat^2) + eps))
+ *             + sum_j FFN_shared_j(x)                    ([H][L] bf16; shared bank,
+ *                                                         hidden = H, weight 1 each)
+ * Dense products are bf16 x fp32 with fp32 sums; the experts run in the
+ * library's expert paths.  All pointers are device pointers owned by the
+ * caller; w_down, w_up and norm_gamma 16-byte aligned. */
+typedef struct {
+  int32_t hidden;               /* H                                          */
+  const float *w_router;        /* [E][H] fp32, E = routed.num_experts        */
+  const uint16_t *w_down;       /* [L][H] bf16 (routed_down), L = routed.hidden */
+  const float *norm_gamma;      /* [L] fp32 (routed_norm weight)              */
+  float norm_eps;               /* routed_norm epsilon, >= 0                  */
+  const uint16_t *w_up;         /* [H][L] bf16 (routed_up)                    */
+  moe_bank routed;              /* routed experts in the latent space          */
+  moe_bank shared;              /* shared experts (hidden = H), 1 .. 32 of them */
+} moe_latent_layer;
+
+/* Workspace bytes for moe_latent_layer_fwd (0 outside the supported range:
+ * 1 <= C <= MOE_MAX_DECODE_TOKENS, 1 <= k <= min(E, MOE_MAX_TOPK)). */
+size_t moe_latent_workspace_size(const moe_latent_layer *layer, int32_t top_k, int32_t C);
+
+/* The whole latent layer for C <= MOE_MAX_DECODE_TOKENS tokens.
+ *  x [C][H] fp32 in (16-byte aligned); out [C][H] fp32 out (may not alias x).
+ *  topk_idx_out / topk_w_out ([C][k]) may be NULL; when given they receive
+ *  the routed selection.  The workspace must have been initialised with
+ *  moe_workspace_init; its uint32 at byte offset 16 is the error word of the
+ *  single-launch expert kernel, as for moe_expert_fwd.  Returns
+ *  MOE_ERR_UNSUPPORTED for shapes outside: H and L multiples of 32, shared
+ *  bank hidden = H, 1 .. 32 shared experts. */
+moe_status moe_latent_layer_fwd(const moe_latent_layer *layer, const float *x, int32_t C,
+                                int32_t k, float *out, int32_t *topk_idx_out, float *topk_w_out,
+                                void *ws, size_t ws_bytes, void *stream);
+
 /* Test export: dequantise one matrix of one expert to fp32.
  *  matrix 0 = gate [I][H], 1 = up [I][H], 2 = down [H][I].
  *  MXFP4: w = e2m1 * 2^(b-127), exact (IEEE denormals kept).

@@ -236,6 +236,58 @@ def layer(spec: synth.BankSpec, Wr: np.ndarray, x: np.ndarray, k: int,
 
 
 # ---------------------------------------------------------------------------
+# Latent MoE layer
+# ---------------------------------------------------------------------------
+# Page "SparkInfer-K3", section "How the TP module works": the router, routed_down
+# (hidden to latent) and the routed experts form the partial phase; routed_norm,
+# routed_up (latent to hidden) and the shared experts form the finish phase.
+# Section "Why the reduce is at 3584 and not 7168": the RMS norm acts on the
+# sum of the routed experts' outputs.  Section "The model": 2 shared experts,
+# latent width 3584, expert FFN 3072.  The shared experts see the hidden x and
+# enter with weight 1 each (the pages give them no gate).
+def bf16_matrix(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns -> their exact values in fp64."""
+    b = np.asarray(bits, np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def dense(W_bits: np.ndarray, x: np.ndarray) -> np.ndarray:
+    """y [C][N] = x [C][K] times W^T for a bf16 matrix W [N][K], in fp64."""
+    return np.asarray(x, np.float64) @ bf16_matrix(W_bits).T
+
+
+def rms_norm(y: np.ndarray, gamma: np.ndarray, eps: float) -> np.ndarray:
+    """gamma * y / sqrt(mean(y^2) + eps), row by row, in fp64."""
+    y = np.asarray(y, np.float64)
+    ms = np.mean(y * y, axis=-1, keepdims=True)
+    return np.asarray(gamma, np.float64) * y / np.sqrt(ms + float(eps))
+
+
+def latent_layer(wl: synth.LatentWorkload, Wr: np.ndarray, x: np.ndarray, Wd_bits: np.ndarray,
+                 Wu_bits: np.ndarray, gamma: np.ndarray, idx: np.ndarray | None = None,
+                 layer: int = 0, routed_cache: dict | None = None,
+                 shared_cache: dict | None = None):
+    """One latent MoE layer for x [C][H].  With ``idx`` given, that routed
+    selection is evaluated (weights still the oracle's for it).  The routed
+    experts take x_lat as fp32, as every expert input is."""
+    C = x.shape[0]
+    L = router_logits(x, Wr)
+    if idx is None:
+        idx = topk(L, wl.k)
+    idx = np.asarray(idx, np.int32)
+    w = np.stack([route_weights(L[t, idx[t]]) for t in range(C)])
+    xlat = dense(Wd_bits, x)
+    ylat = experts_forward(wl.routed_bank(layer), xlat.astype(np.float32), idx, w, routed_cache)
+    yn = rms_norm(ylat, gamma, wl.eps)
+    routed = dense(Wu_bits, yn)
+    sidx = np.tile(np.arange(wl.n_shared, dtype=np.int32), (C, 1))
+    shared = experts_forward(wl.shared_bank(layer), x, sidx, np.ones((C, wl.n_shared)),
+                             shared_cache)
+    return {"logits": L, "idx": idx, "w": w, "xlat": xlat, "ylat": ylat, "routed": routed,
+            "shared": shared, "out": routed + shared}
+
+
+# ---------------------------------------------------------------------------
 # Comparison helpers
 # ---------------------------------------------------------------------------
 def rel_l2(got: np.ndarray, ref: np.ndarray) -> float:

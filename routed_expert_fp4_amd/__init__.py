@@ -25,7 +25,8 @@ MOE_MAX_EXPERTS, MOE_MAX_TOPK, MOE_MAX_DECODE_TOKENS, MOE_MAX_TOKENS = 1024, 32,
 BLOCK = {MOE_FMT_MXFP4: 32, MOE_FMT_NVFP4: 16}
 
 EXPORTS = ("moe_version", "moe_status_string", "moe_bank_layout", "moe_workspace_size",
-           "moe_workspace_init", "moe_route", "moe_expert_fwd", "moe_layer_fwd", "moe_dequant")
+           "moe_workspace_init", "moe_route", "moe_expert_fwd", "moe_layer_fwd", "moe_dequant",
+           "moe_latent_workspace_size", "moe_latent_layer_fwd")
 
 
 class MoeError(RuntimeError):
@@ -39,6 +40,13 @@ class moe_bank(ctypes.Structure):
                 ("hidden", ctypes.c_int32), ("inter", ctypes.c_int32),
                 ("base", ctypes.c_void_p), ("expert_stride", ctypes.c_int64),
                 ("offset", ctypes.c_int64 * MOE_NUM_TENSORS)]
+
+
+class moe_latent_layer(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("w_router", ctypes.c_void_p),
+                ("w_down", ctypes.c_void_p), ("norm_gamma", ctypes.c_void_p),
+                ("norm_eps", ctypes.c_float), ("w_up", ctypes.c_void_p),
+                ("routed", moe_bank), ("shared", moe_bank)]
 
 
 _lib = None
@@ -63,6 +71,8 @@ def lib() -> ctypes.CDLL:
             "moe_expert_fwd": ([P, P, i32, i32, P, P, P, P, sz, P], i32),
             "moe_layer_fwd": ([P, P, P, i32, i32, P, P, P, P, sz, P], i32),
             "moe_dequant": ([P, i32, i32, P, P], i32),
+            "moe_latent_workspace_size": ([P, i32, i32], sz),
+            "moe_latent_layer_fwd": ([P, P, i32, i32, P, P, P, P, sz, P], i32),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -209,3 +219,56 @@ def moe_dequant(bank: Bank, expert: int, matrix: int, out, stream=None):
     N, K = (bank.H, bank.I) if matrix == 2 else (bank.I, bank.H)
     _check("moe_dequant", lib().moe_dequant(_bank(bank), expert, matrix,
                                             _ptr(out, torch.float32, (N, K), "out"), _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+# Latent MoE layer (routed_down, routed experts, routed_norm, routed_up, shared)
+# ---------------------------------------------------------------------------
+class LatentLayer:
+    """The device tensors of one latent MoE layer and its moe_latent_layer struct.
+    w_router [E][H] fp32, w_down [L][H] and w_up [H][L] as int16/uint16 bf16
+    bits, gamma [L] fp32; routed (hidden L) and shared (hidden H) are Banks."""
+
+    def __init__(self, w_router, w_down, gamma, eps: float, w_up, routed: Bank, shared: Bank):
+        import torch
+        H, L = shared.H, routed.H
+        _ptr(w_router, torch.float32, (routed.E, H), "w_router")
+        if w_down.dtype not in (torch.int16, torch.uint16) or tuple(w_down.shape) != (L, H):
+            raise ValueError(f"w_down must be bf16 bits of shape {(L, H)}")
+        if w_up.dtype not in (torch.int16, torch.uint16) or tuple(w_up.shape) != (H, L):
+            raise ValueError(f"w_up must be bf16 bits of shape {(H, L)}")
+        _ptr(gamma, torch.float32, (L,), "gamma")
+        self.keep = (w_router, w_down, gamma, w_up, routed, shared)
+        self.H, self.L, self.E = H, L, routed.E
+        self.struct = moe_latent_layer(H, w_router.data_ptr(), _ptr(w_down, name="w_down").value,
+                                       gamma.data_ptr(), eps, _ptr(w_up, name="w_up").value,
+                                       routed.struct, shared.struct)
+
+
+class LatentWorkspace:
+    def __init__(self, layer: LatentLayer, top_k: int, C: int, device="cuda", stream=None):
+        import torch
+        n = lib().moe_latent_workspace_size(ctypes.byref(layer.struct), top_k, C)
+        if n == 0:
+            raise MoeError("moe_latent_workspace_size", MOE_ERR_UNSUPPORTED)
+        self.tensor = torch.empty((n + 255) // 256 * 256 // 4, dtype=torch.int32, device=device)
+        moe_workspace_init(self.tensor, stream)
+
+    @property
+    def ptr(self):
+        return ctypes.c_void_p(self.tensor.data_ptr())
+
+    @property
+    def nbytes(self):
+        return self.tensor.numel() * 4
+
+
+def moe_latent_layer_fwd(layer: LatentLayer, x, C, k, out, topk_idx_out=None, topk_w_out=None,
+                         ws: LatentWorkspace = None, stream=None):
+    import torch
+    H = layer.H
+    _check("moe_latent_layer_fwd", lib().moe_latent_layer_fwd(
+        ctypes.byref(layer.struct), _ptr(x, torch.float32, (C, H), "x"), C, k,
+        _ptr(out, torch.float32, (C, H), "out"),
+        _ptr(topk_idx_out, torch.int32, (C, k), "topk_idx_out"),
+        _ptr(topk_w_out, torch.float32, (C, k), "topk_w_out"), ws.ptr, ws.nbytes, _stream(stream)))

@@ -263,6 +263,77 @@ WORKLOADS = {
 }
 
 
+# ----------------------------------------------------------------------------
+# Latent MoE layer (routed_down, routed experts, routed_norm, routed_up, shared)
+# ----------------------------------------------------------------------------
+S_DOWN, S_UP, S_GAMMA = 11, 12, 13
+
+
+def dense_bf16(seed: int, layer: int, stream: int, N: int, K: int) -> np.ndarray:
+    """A dense [N][K] matrix of N(0, 1/K) entries rounded to bf16, as uint16 bits."""
+    g = rng_for(seed, layer, stream)
+    a = g.standard_normal((N, K), dtype=np.float32) * np.float32(1.0 / math.sqrt(K))
+    return (round_to_bf16(a).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (np.asarray(b, np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+@dataclasses.dataclass(frozen=True)
+class LatentWorkload:
+    """A latent MoE layer: router on the hidden x (H), routed experts in the
+    latent space (L, FFN I), n_shared shared experts on x (H, FFN I_shared).
+    The norm's gamma is gamma_scale * (1 + 0.1 N(0, 1)): the synthetic banks'
+    expert outputs are large, and gamma_scale (a power of two near the shared
+    part's RMS) brings the normalised routed part to the same size, as a
+    trained norm weight would."""
+    name: str
+    fmt: int
+    E: int
+    k: int
+    H: int
+    L: int
+    I: int
+    n_shared: int
+    I_shared: int
+    C: int
+    layers: int = 1
+    eps: float = 1e-6
+    gamma_scale: float = 1.0
+    seed: int = 0
+
+    def routed_bank(self, layer: int = 0) -> BankSpec:
+        return BankSpec(self.fmt, self.E, self.L, self.I, self.seed, layer)
+
+    def shared_bank(self, layer: int = 0) -> BankSpec:
+        return BankSpec(self.fmt, self.n_shared, self.H, self.I_shared, self.seed + 1, layer)
+
+    def with_(self, **kw) -> "LatentWorkload":
+        return dataclasses.replace(self, **kw)
+
+
+LATENT_WORKLOADS = {
+    # page "SparkInfer-K3", section "The model": 896 routed experts, top-16,
+    # 2 shared, latent 3584, expert FFN 3072, hidden 7168
+    "k3_latent": LatentWorkload("k3_latent", FMT_NV, 896, 16, 7168, 3584, 3072, 2, 3072, 1, 4,
+                                gamma_scale=2.0 ** 20),
+}
+
+
+def latent_inputs(w: LatentWorkload, layer: int, pool: int = 0, C: int | None = None):
+    """(W_r [E][H] fp32, x [C][H] fp32, W_down [L][H] bf16 bits, W_up [H][L]
+    bf16 bits, gamma [L] fp32) of one latent layer."""
+    C = w.C if C is None else C
+    Wr = router_weights(w.seed, layer, w.E, w.H)
+    x = activations(w.seed, layer, C, w.H, pool)
+    Wd = dense_bf16(w.seed, layer, S_DOWN, w.L, w.H)
+    Wu = dense_bf16(w.seed, layer, S_UP, w.H, w.L)
+    g = rng_for(w.seed, layer, S_GAMMA)
+    gamma = (w.gamma_scale * (1.0 + 0.1 * g.standard_normal(w.L))).astype(np.float32)
+    return Wr, x, Wd, Wu, gamma
+
+
 def layer_inputs(w: Workload, layer: int, pool: int = 0, C: int | None = None):
     """(W_r, x) of one layer of a workload; x steered for Zipf routing and
     rounded to bf16 when the workload says so."""
