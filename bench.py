@@ -252,8 +252,14 @@ def bench_latent(args, wl):
     alg_bytes = uniq * rexp + wl.n_shared * sexp + dense_bytes + 2 * C * wl.H * 4
     gbps = alg_bytes / (us_call * 1e-6) / 1e9
     fmt = "nvfp4" if wl.fmt == synth.FMT_NV else "mxfp4"
-    routed_kernel = "k_moe1 (routed experts, selection given)" if C == 1 else \
-        "k_dispatch + k_dstream<GU> + k_dstream<DN> + k_bcombine (routed experts)"
+    if C == 1:
+        kernels = ("k_gemv (routed_down, with the shared selection), k_moe1 (router on the hidden "
+                   "state + routed experts, one launch), shared experts (k_dispatch + "
+                   "k_dstream<GU> + k_dstream<DN> + k_bcombine), k_gemv (norm + routed_up)")
+    else:
+        kernels = ("k_gemv (routed_down, with the shared selection), k_route + k_btopk (router), "
+                   "routed experts and then shared experts (k_dispatch + k_dstream<GU> + "
+                   "k_dstream<DN> + k_bcombine each), k_gemv (norm + routed_up)")
     result = {
         "metric": "latent MoE layer decode µs/token + achieved HBM GB/s (% of peak)",
         "value": round(us_call / C, 3),
@@ -276,9 +282,7 @@ def bench_latent(args, wl):
         "distinct_experts_per_call": round(float(uniq), 2),
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
-                     "kernel": "k_route + k_btopk (router), k_gemv (routed_down), " + routed_kernel
-                               + ", k_shared_sel + shared experts, k_gemv (norm + routed_up) "
-                               "per moe_latent_layer_fwd call",
+                     "kernel": kernels + " per moe_latent_layer_fwd call",
                      "bytes_per_launch": int(alg_bytes), "us_per_launch": round(us_call, 3)},
         "wall_s_timed": round(wall, 3),
     }

@@ -19,6 +19,11 @@ page "SparkInfer-K3", section "How the TP module works" (router, the chosen
 top-16, the sum of the expert outputs); page "Kimi-K3 on the same pod, two
 engines", section "Reason 1" (partial sums added in a fixed order).
 
+The latent layer (``latent_layer``) adds, with numpy in fp64: routed_down and
+routed_up as bf16 dense products, and the RMS norm of the routed sum (page
+"SparkInfer-K3", sections "How the TP module works" and "Why the reduce is at
+3584 and not 7168").  The shared experts reuse the expert FFN at weight 1.
+
 Every function is pinned by tests in ``tests/test_oracle_*.py`` against closed
 forms, exact rational arithmetic, brute force and library routines.
 """

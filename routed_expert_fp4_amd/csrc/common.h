@@ -328,5 +328,14 @@ bool batched_decode_shape(const moe_bank* b, int C);
 moe_status launch_batched_decode(const moe_bank* b, const float* x, int C, int k,
                                  const int32_t* idx, const float* w, float* out, uint8_t* ws,
                                  const WsLayout& L, hipStream_t st);
+// layer1_router_input: one token through a layer whose router reads an input
+// of its own, xr [Hr] against w_router [E][Hr], while the experts take x [H]
+// (a latent layer: routed on the hidden state, experts in the latent width).
+// The single-launch kernel when the bank's shape is built for it; otherwise
+// MOE_ERR_UNSUPPORTED with nothing enqueued.  ws is the bank's workspace
+// (ws_layout(E, H, I, k, 1)).
+moe_status layer1_router_input(const moe_bank* b, const float* w_router, const float* xr, int Hr,
+                               const float* x, int k, float* out, int32_t* idx, float* w,
+                               void* ws, size_t ws_bytes, hipStream_t st);
 
 }  // namespace rf4

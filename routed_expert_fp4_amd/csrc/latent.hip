@@ -19,9 +19,9 @@
 // Kernels:
 //   k_gemv      y[t] (+)= s_t * W (g * x[t]) for C <= 16 tokens: bf16 W [N][K],
 //               fp32 x [C][K]; with g (the norm's gamma) the row scale s_t is
-//               1 / rms(x[t]), else s_t = 1 and g = 1
-//   k_shared_sel the shared experts' selection: every token, every shared
-//               expert, weight 1
+//               1 / rms(x[t]), else s_t = 1 and g = 1.  The routed_down launch
+//               also writes the shared experts' selection (every token, every
+//               shared expert, weight 1).
 #include "common.h"
 
 namespace rf4 {
@@ -35,113 +35,164 @@ struct GemvArgs {
   float* y;               // [C][N]
   int C, N, K;
   int accumulate;         // 1: y += result
+  int32_t* sel_idx;       // or null: [C][ns] shared-expert selection to write
+  float* sel_w;
+  int ns;
 };
 
-constexpr int kGemvRows = 2;             // output rows per wave
 constexpr int kGemvWG = 256;
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// Each wave takes kGemvRows rows for every token; a lane reads 16 bytes (8
-// weights) of a row at a time, rows along K, and the x tile of the current K
-// chunk (all tokens) sits in LDS.  With the norm, every workgroup first sums
-// each token's squares over all of K (wave t % 4 takes token t), and gamma is
-// applied to x as it is staged; 1 / rms multiplies the finished dot product.
-template <int CM>
-__global__ __launch_bounds__(kGemvWG) void k_gemv(GemvArgs a) {
-  constexpr int KT = kRouteXs / CM;                   // staged floats per token per chunk
-  __shared__ float xs[kRouteXs];
-  __shared__ float s_rs[CM];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int C = a.C, K = a.K, N = a.N;
-  const int n0 = (blockIdx.x * (kGemvWG / 64) + wave) * kGemvRows;
+// Sum over the wave with DPP row shifts and row broadcasts; every lane gets
+// lane 63's total.
+template <int CTRL, int RMASK>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, RMASK, 0xF, false));
+}
 
-  if (a.gamma) {
-    for (int t = wave; t < C; t += kGemvWG / 64) {
-      float ss = 0.0f;
-      for (int i = lane * 4; i < K; i += 64 * 4) {
-        const float4 v = *reinterpret_cast<const float4*>(a.x + (size_t)t * K + i);
-        ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
-      }
-      ss = wave_sum(ss);
-      if (lane == 0) s_rs[t] = 1.0f / sqrtf(ss / (float)K + a.eps);
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v += dpp_f<0x111, 0xF>(v);   // row_shr:1
+  v += dpp_f<0x112, 0xF>(v);   // row_shr:2
+  v += dpp_f<0x114, 0xF>(v);   // row_shr:4
+  v += dpp_f<0x118, 0xF>(v);   // row_shr:8
+  v += dpp_f<0x142, 0xA>(v);   // row_bcast:15
+  v += dpp_f<0x143, 0xC>(v);   // row_bcast:31
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+// RB rows per workgroup, the whole K: the 256 threads split each row into
+// 16-byte chunks (8 bf16), NCH chunks per thread per slab of 2048 * NCH
+// elements; every weight load of a slab is issued before any arithmetic, and x
+// (with gamma applied) comes straight from L2 into registers for each chunk, in
+// groups of up to 4 tokens.  With the norm, the same x values give each
+// token's sum of squares over K.  The per-thread partial sums are reduced over
+// the wave (DPP) and then over the four waves in order.
+template <int RB, int CM, int NCH>
+__global__ __launch_bounds__(kGemvWG) void k_gemv(GemvArgs a) {
+  constexpr int TG = CM < 4 ? CM : 4;                 // tokens per x group
+  __shared__ float s_part[kGemvWG / 64][RB * CM + CM];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int C = a.C, K = a.K, N = a.N, K8 = K >> 3;
+  const int n0 = blockIdx.x * RB;
+  const bool norm = a.gamma != nullptr;
+
+  if (a.sel_idx && blockIdx.x == 0) {
+    for (int i = tid; i < C * a.ns; i += kGemvWG) {
+      a.sel_idx[i] = i % a.ns;
+      a.sel_w[i] = 1.0f;
     }
   }
 
-  float acc[kGemvRows][CM];
+  float acc[RB][CM], ss[CM];
 #pragma unroll
-  for (int r = 0; r < kGemvRows; ++r)
+  for (int t = 0; t < CM; ++t) {
+    ss[t] = 0.0f;
 #pragma unroll
-    for (int t = 0; t < CM; ++t) acc[r][t] = 0.0f;
+    for (int r = 0; r < RB; ++r) acc[r][t] = 0.0f;
+  }
 
-  for (int kt = 0; kt < K; kt += KT) {
-    const int kn = min(KT, K - kt);
-    __syncthreads();
-    for (int i = tid * 4; i < C * kn; i += kGemvWG * 4) {
-      const int t = i / kn, col = i - t * kn;
-      float4 v = *reinterpret_cast<const float4*>(a.x + (size_t)t * K + kt + col);
-      if (a.gamma) {
-        const float4 g = *reinterpret_cast<const float4*>(a.gamma + kt + col);
-        v.x *= g.x; v.y *= g.y; v.z *= g.z; v.w *= g.w;
+  for (int c0 = 0; c0 < K8; c0 += kGemvWG * NCH) {
+    uint4 wq[RB][NCH];
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+      const int c = c0 + tid + kGemvWG * j;
+#pragma unroll
+      for (int r = 0; r < RB; ++r) {
+        const int n = n0 + r;
+        wq[r][j] = (c < K8 && n < N)
+                       ? reinterpret_cast<const uint4*>(a.W + (size_t)n * K)[c]
+                       : make_uint4(0u, 0u, 0u, 0u);
       }
-      *reinterpret_cast<float4*>(&xs[t * KT + col]) = v;
     }
-    __syncthreads();
-    const int n8 = kn >> 3;                           // 16-byte chunks of a row in this K chunk
 #pragma unroll
-    for (int r = 0; r < kGemvRows; ++r) {
-      const int n = n0 + r;
-      if (n >= N) break;
-      const uint4* wrow = reinterpret_cast<const uint4*>(a.W + (size_t)n * K + kt);
-      for (int c = lane; c < n8; c += 64) {
-        const uint4 wq = wrow[c];
-        const float w0 = bf16_lo(wq.x), w1 = bf16_hi(wq.x), w2 = bf16_lo(wq.y), w3 = bf16_hi(wq.y);
-        const float w4 = bf16_lo(wq.z), w5 = bf16_hi(wq.z), w6 = bf16_lo(wq.w), w7 = bf16_hi(wq.w);
+    for (int j = 0; j < NCH; ++j) {
+      const int c = c0 + tid + kGemvWG * j;
+      if (c >= K8) break;
+      float4 ga = make_float4(1.f, 1.f, 1.f, 1.f), gb = ga;
+      if (norm) {
+        ga = *reinterpret_cast<const float4*>(a.gamma + 8 * c);
+        gb = *reinterpret_cast<const float4*>(a.gamma + 8 * c + 4);
+      }
 #pragma unroll
-        for (int t = 0; t < CM; ++t) {
-          if (t >= C) break;
-          const float4 xa = *reinterpret_cast<const float4*>(&xs[t * KT + 8 * c]);
-          const float4 xb = *reinterpret_cast<const float4*>(&xs[t * KT + 8 * c + 4]);
-          float s = acc[r][t];
-          s += w0 * xa.x; s += w1 * xa.y; s += w2 * xa.z; s += w3 * xa.w;
-          s += w4 * xb.x; s += w5 * xb.y; s += w6 * xb.z; s += w7 * xb.w;
-          acc[r][t] = s;
+      for (int t0 = 0; t0 < CM; t0 += TG) {
+        if (t0 >= C) break;
+        float4 xa[TG], xb[TG];
+#pragma unroll
+        for (int u = 0; u < TG; ++u) {
+          const int t = t0 + u < C ? t0 + u : t0;
+          xa[u] = *reinterpret_cast<const float4*>(a.x + (size_t)t * K + 8 * c);
+          xb[u] = *reinterpret_cast<const float4*>(a.x + (size_t)t * K + 8 * c + 4);
+        }
+#pragma unroll
+        for (int u = 0; u < TG; ++u) {
+          if (t0 + u >= C) break;
+          float4 p = xa[u], q = xb[u];
+          if (norm) {
+            float s = ss[t0 + u];
+            s += p.x * p.x; s += p.y * p.y; s += p.z * p.z; s += p.w * p.w;
+            s += q.x * q.x; s += q.y * q.y; s += q.z * q.z; s += q.w * q.w;
+            ss[t0 + u] = s;
+            p.x *= ga.x; p.y *= ga.y; p.z *= ga.z; p.w *= ga.w;
+            q.x *= gb.x; q.y *= gb.y; q.z *= gb.z; q.w *= gb.w;
+          }
+#pragma unroll
+          for (int r = 0; r < RB; ++r) {
+            const uint4 w = wq[r][j];
+            float s = acc[r][t0 + u];
+            s += bf16_lo(w.x) * p.x; s += bf16_hi(w.x) * p.y;
+            s += bf16_lo(w.y) * p.z; s += bf16_hi(w.y) * p.w;
+            s += bf16_lo(w.z) * q.x; s += bf16_hi(w.z) * q.y;
+            s += bf16_lo(w.w) * q.z; s += bf16_hi(w.w) * q.w;
+            acc[r][t0 + u] = s;
+          }
         }
       }
     }
   }
 
 #pragma unroll
-  for (int r = 0; r < kGemvRows; ++r) {
-    const int n = n0 + r;
+  for (int t = 0; t < CM; ++t) {
+    if (t < C) {
 #pragma unroll
-    for (int t = 0; t < CM; ++t) {
-      if (t >= C) break;
-      const float v = wave_sum(acc[r][t]);
-      if (lane == 0 && n < N) {
-        const float s = a.gamma ? s_rs[t] * v : v;
-        float* yp = a.y + (size_t)t * N + n;
-        *yp = a.accumulate ? *yp + s : s;
+      for (int r = 0; r < RB; ++r) {
+        const float v = wave_sum_dpp(acc[r][t]);
+        if (lane == 0) s_part[wave][r * CM + t] = v;
       }
+      if (norm) {
+        const float v = wave_sum_dpp(ss[t]);
+        if (lane == 0) s_part[wave][RB * CM + t] = v;
+      }
+    }
+  }
+  __syncthreads();
+  if (tid < RB * C) {
+    const int r = tid / C, t = tid - r * C, n = n0 + r;
+    if (n < N) {
+      const int i = r * CM + t;
+      float v = ((s_part[0][i] + s_part[1][i]) + s_part[2][i]) + s_part[3][i];
+      if (norm) {
+        const int j = RB * CM + t;
+        const float sq = ((s_part[0][j] + s_part[1][j]) + s_part[2][j]) + s_part[3][j];
+        v *= 1.0f / sqrtf(sq / (float)K + a.eps);
+      }
+      float* yp = a.y + (size_t)t * N + n;
+      *yp = a.accumulate ? *yp + v : v;
     }
   }
 }
 
-__global__ void k_shared_sel(int32_t* idx, float* w, int C, int ns) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < C * ns) {
-    idx[i] = i % ns;
-    w[i] = 1.0f;
-  }
+template <int RB, int CM, int NCH>
+void launch_gemv_t(const GemvArgs& a, hipStream_t st) {
+  const int grid = (a.N + RB - 1) / RB;
+  hipLaunchKernelGGL((k_gemv<RB, CM, NCH>), dim3(grid), dim3(kGemvWG), 0, st, a);
 }
 
 moe_status launch_gemv(const GemvArgs& a, hipStream_t st) {
-  const int waves = (a.N + kGemvRows - 1) / kGemvRows;
-  const int grid = (waves + kGemvWG / 64 - 1) / (kGemvWG / 64);
-  if (a.C <= 1) hipLaunchKernelGGL(k_gemv<1>, dim3(grid), dim3(kGemvWG), 0, st, a);
-  else if (a.C <= 4) hipLaunchKernelGGL(k_gemv<4>, dim3(grid), dim3(kGemvWG), 0, st, a);
-  else hipLaunchKernelGGL(k_gemv<16>, dim3(grid), dim3(kGemvWG), 0, st, a);
+  if (a.C <= 1) launch_gemv_t<8, 1, 4>(a, st);
+  else if (a.C <= 4) launch_gemv_t<4, 4, 4>(a, st);
+  else launch_gemv_t<4, 16, 2>(a, st);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_DEVICE;
 }
 
@@ -223,22 +274,30 @@ moe_status moe_latent_layer_fwd(const moe_latent_layer* layer, const float* x, i
   const size_t wr_bytes = W.route - W.routed, wq_bytes = W.shared - W.route,
                ws_bytes_s = W.xlat - W.shared;
 
-  // partial phase: router on x, routed_down, routed experts
-  moe_status s = moe_route(x, layer->w_router, nullptr, C, H, R.num_experts, k, idx, w, w8 + W.route,
-                           wq_bytes, stream);
-  if (s != MOE_OK) return s;
+  // partial phase: routed_down, then the router on x and the routed experts
+  // on x_lat (one launch for one token where the bank's shape is built for
+  // the single-launch kernel, else the router and the expert path apart)
   GemvArgs g;
   g.W = layer->w_down; g.x = x; g.gamma = nullptr; g.eps = 0.0f; g.y = xlat;
   g.C = C; g.N = L; g.K = H; g.accumulate = 0;
-  if ((s = launch_gemv(g, st)) != MOE_OK) return s;
-  s = moe_expert_fwd(&R, xlat, C, k, idx, w, ylat, wr, wr_bytes, stream);
+  g.sel_idx = sidx; g.sel_w = sw; g.ns = ns;     // the shared experts' selection
+  moe_status s = launch_gemv(g, st);
+  if (s != MOE_OK) return s;
+  s = C == 1 ? layer1_router_input(&R, layer->w_router, x, H, xlat, k, ylat, idx, w, wr, wr_bytes, st)
+             : MOE_ERR_UNSUPPORTED;
+  if (s == MOE_ERR_UNSUPPORTED) {
+    s = moe_route(x, layer->w_router, nullptr, C, H, R.num_experts, k, idx, w, w8 + W.route,
+                  wq_bytes, stream);
+    if (s != MOE_OK) return s;
+    s = moe_expert_fwd(&R, xlat, C, k, idx, w, ylat, wr, wr_bytes, stream);
+  }
   if (s != MOE_OK) return s;
   // finish phase: shared experts into out, then routed_norm and routed_up added
-  hipLaunchKernelGGL(k_shared_sel, dim3((C * ns + 255) / 256), dim3(256), 0, st, sidx, sw, C, ns);
   s = moe_expert_fwd(&S, x, C, ns, sidx, sw, out, w8 + W.shared, ws_bytes_s, stream);
   if (s != MOE_OK) return s;
   g.W = layer->w_up; g.x = ylat; g.gamma = layer->norm_gamma; g.eps = layer->norm_eps; g.y = out;
   g.C = C; g.N = H; g.K = L; g.accumulate = 1;
+  g.sel_idx = nullptr; g.sel_w = nullptr; g.ns = 0;
   return launch_gemv(g, st);
 }
 

@@ -784,8 +784,8 @@ struct Moe1Args {
   int64_t stride;
   int64_t off[MOE_NUM_TENSORS];
   int E, H, I, k;
-  const float* x;          // [H]
-  const float* Wr;         // [E][H], or null: selection given in idx_in / w_in
+  const float* x;          // [H] expert input (and the router's, unless XR)
+  const float* Wr;         // [E][H] (XR: [E][Hr]), or null: selection given in idx_in / w_in
   const int32_t* idx_in;   // [k]
   const float* w_in;       // [k]
   int32_t* idx_out;        // [k] or null
@@ -796,6 +796,8 @@ struct Moe1Args {
   float* out;              // [H]
   uint32_t* ctrl;
   int n_router;
+  const float* xr;         // XR instances: the router's own input [Hr]
+  int Hr;
 };
 
 struct Moe1Shared {
@@ -839,12 +841,14 @@ __device__ __forceinline__ int router_half_row(const Moe1Args& a) {
 // Every load is issued (those past the half row, or of a wave without one,
 // fall outside the view and read zeros), so the loads form one straight run
 // and later waits can count them exactly.
+template <bool XR>
 __device__ __forceinline__ void moe1_router_load(const Moe1Args& a, int hr, float4 (&wv)[kRouterRU]) {
   const int lane = threadIdx.x & 63;
-  const int q = a.H / 2;                          // columns per half row
+  const int Hr = XR ? a.Hr : a.H;
+  const int q = Hr / 2;                           // columns per half row
   const int e = hr >= 0 ? hr >> 1 : 0, half = hr & 1;
   const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<float*>(hr >= 0 ? a.Wr + (size_t)e * a.H : a.x), (short)0, hr >= 0 ? a.H * 4 : 0,
+      const_cast<float*>(hr >= 0 ? a.Wr + (size_t)e * Hr : a.x), (short)0, hr >= 0 ? Hr * 4 : 0,
       0x00020000);
   const uint32_t woff = (uint32_t)(half * q + lane * 4) * 4;
 #pragma unroll
@@ -857,10 +861,11 @@ __device__ __forceinline__ void moe1_router_load(const Moe1Args& a, int hr, floa
   }
 }
 
+template <bool XR>
 __device__ __forceinline__ void moe1_router_finish(const Moe1Args& a, Moe1Shared& S, int hr,
                                                    const float4 (&wv)[kRouterRU], uint32_t epoch) {
   const int lane = threadIdx.x & 63;
-  const int q = a.H / 2;
+  const int q = (XR ? a.Hr : a.H) / 2;
   if (hr < 0) return;                             // whole waves
   const int e = hr >> 1, half = hr & 1;
   float acc = 0.0f;
@@ -881,7 +886,7 @@ __device__ __forceinline__ void moe1_router_finish(const Moe1Args& a, Moe1Shared
 // logits (or taken from the caller when the selection is given): all eight
 // waves poll and gather the candidates above a threshold, wave 0 ranks them
 // (the same exact top-k as wave_select, which remains the fallback).
-__device__ void moe1_routing(const Moe1Args& a, Moe1Shared& S, uint32_t epoch, bool writer) {
+__device__ __forceinline__ void moe1_routing(const Moe1Args& a, Moe1Shared& S, uint32_t epoch, bool writer) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int k = a.k;
   constexpr int NPL = MOE_MAX_EXPERTS / 64;
@@ -1128,7 +1133,7 @@ struct SegStream {
 // Gate/up slice: rows b*16*SGU + lg + 16*s (s < SGU) of slot u's expert;
 // h = silu(g) * u goes out as tagged words.
 template <int FMT, int KG, int SGU>
-__device__ void moe1_gate_up_slice(const Moe1Args& a, Moe1Shared& S, int u, int b, uint32_t epoch) {
+__device__ __forceinline__ void moe1_gate_up_slice(const Moe1Args& a, Moe1Shared& S, int u, int b, uint32_t epoch) {
   const int e = S.sidx[u];
   if (e < 0 || e >= a.E) return;                 // an invalid slot contributes nothing
   const int lg = threadIdx.x >> 4, l16 = threadIdx.x & 15;
@@ -1173,7 +1178,7 @@ __device__ void moe1_gate_up_slice(const Moe1Args& a, Moe1Shared& S, int u, int 
 // slot) of slot u's expert, against h_u; the results go out as tagged words,
 // or, for the last slot, to LDS for the combine.
 template <int FMT, int KD, int SDN, int KT>
-__device__ void moe1_down_slice(const Moe1Args& a, Moe1Shared& S, int u, int b, int R,
+__device__ __forceinline__ void moe1_down_slice(const Moe1Args& a, Moe1Shared& S, int u, int b, int R,
                                 uint32_t epoch, bool xcd_local) {
   const int e = S.sidx[u];
   const bool valid = e >= 0 && e < a.E;
@@ -1253,7 +1258,7 @@ __device__ void moe1_down_slice(const Moe1Args& a, Moe1Shared& S, int u, int b, 
 // (they are written at each workgroup's start, so normally all are there);
 // any that were not are polled again here.
 template <int KT>
-__device__ void moe1_combine(const Moe1Args& a, Moe1Shared& S, uint32_t epoch, uint32_t arrived) {
+__device__ __forceinline__ void moe1_combine(const Moe1Args& a, Moe1Shared& S, uint32_t epoch, uint32_t arrived) {
   const int H = a.H, RC = H / kG1;
   const int j0 = blockIdx.x * RC, tid = threadIdx.x;
   const int sl = tid / RC, r = tid - sl * RC;
@@ -1311,8 +1316,10 @@ __device__ void moe1_combine(const Moe1Args& a, Moe1Shared& S, uint32_t epoch, u
 // router -> selection -> gate/up -> down -> combine, so with every workgroup
 // resident each poll ends, and each is bounded anyway.
 // KG = H/512, KD = I/512 (16-byte chunks per lane per row); SGU, SDN: row
-// segments per 16-lane group in the gate/up and down slices.
-template <int FMT, int KG, int KD, int SGU, int SDN, int KT>
+// segments per 16-lane group in the gate/up and down slices.  XR: the router
+// reads an input of its own, xr [Hr] (a latent layer routes on the hidden
+// state while its experts take the latent vector).
+template <int FMT, int KG, int KD, int SGU, int SDN, int KT, bool XR>
 __global__ __launch_bounds__(kWG1, 1) void k_moe1(Moe1Args a) {
   __shared__ Moe1Shared S;
   const int tid = threadIdx.x;
@@ -1326,24 +1333,37 @@ __global__ __launch_bounds__(kWG1, 1) void k_moe1(Moe1Args a) {
 #pragma unroll
   for (int j = 0; j < kXv; ++j) {
     const int i = (tid + j * kWG1) * 4;
-    xv[j] = i < a.H ? *reinterpret_cast<const float4*>(a.x + i) : make_float4(0.f, 0.f, 0.f, 0.f);
+    const int Hr = XR ? a.Hr : a.H;
+    xv[j] = i < Hr ? *reinterpret_cast<const float4*>((XR ? a.xr : a.x) + i)
+                   : make_float4(0.f, 0.f, 0.f, 0.f);
   }
   __builtin_amdgcn_sched_barrier(0);
   float4 wv[kRouterRU];
   const int hr = router_half_row(a);
-  moe1_router_load(a, hr, wv);
+  moe1_router_load<XR>(a, hr, wv);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int j = 0; j < kXv; ++j) {
     const int i = (tid + j * kWG1) * 4;
-    if (i < a.H) *reinterpret_cast<float4*>(&S.u.xs[i + (i >> 5) * 4]) = xv[j];
+    if (i < (XR ? a.Hr : a.H)) *reinterpret_cast<float4*>(&S.u.xs[i + (i >> 5) * 4]) = xv[j];
   }
   // this workgroup has read the epoch (the combine waits for all of these
   // before it publishes the next one)
   if (tid == 0)
     __hip_atomic_store(&a.ctrl[kCtrlArrive + blockIdx.x], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
-  moe1_router_finish(a, S, hr, wv, epoch);
+  moe1_router_finish<XR>(a, S, hr, wv, epoch);
+  if (XR) {
+    // the expert input replaces the router's in LDS for the gate/up slice
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kXv; ++j) {
+      const int i = (tid + j * kWG1) * 4;
+      if (i < a.H)
+        *reinterpret_cast<float4*>(&S.u.xs[i + (i >> 5) * 4]) = *reinterpret_cast<const float4*>(a.x + i);
+    }
+    __syncthreads();
+  }
   moe1_routing(a, S, epoch, blockIdx.x == 0);
   // the arrival words, read early (used by the combine of workgroup 0)
   uint32_t arrived = 0u;
@@ -1561,7 +1581,7 @@ struct Moe1Shape {
   int H, I, k;
 };
 
-template <int FMT, int KG, int KD, int SGU, int SDN, int KT>
+template <int FMT, int KG, int KD, int SGU, int SDN, int KT, bool XR = false>
 moe_status launch_moe1_kernel(Moe1Args a, hipStream_t st) {
   static int ok_dev[64] = {0};   // 1: kG1 workgroups fit at once on this device, -1: they do not
   int dev = 0;
@@ -1569,7 +1589,7 @@ moe_status launch_moe1_kernel(Moe1Args a, hipStream_t st) {
   if (ok_dev[dev] == 0) {
     int per_cu = 0;
     const bool fits = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                          &per_cu, k_moe1<FMT, KG, KD, SGU, SDN, KT>, kWG1, 0) == hipSuccess &&
+                          &per_cu, k_moe1<FMT, KG, KD, SGU, SDN, KT, XR>, kWG1, 0) == hipSuccess &&
                       per_cu * device_cu_count() >= kG1;
     ok_dev[dev] = fits ? 1 : -1;
   }
@@ -1580,7 +1600,7 @@ moe_status launch_moe1_kernel(Moe1Args a, hipStream_t st) {
   // the same guarantee but costs about 17 us more per call on this stack.)
   // Should other work hold CUs indefinitely, the bounded waits give up and set
   // the workspace's error word instead of hanging.
-  hipLaunchKernelGGL((k_moe1<FMT, KG, KD, SGU, SDN, KT>), dim3(kG1), dim3(kWG1), 0, st, a);
+  hipLaunchKernelGGL((k_moe1<FMT, KG, KD, SGU, SDN, KT, XR>), dim3(kG1), dim3(kWG1), 0, st, a);
   const hipError_t err = hipGetLastError();
   if (err != hipSuccess) return MOE_ERR_DEVICE;
   return MOE_OK;
@@ -1589,6 +1609,12 @@ moe_status launch_moe1_kernel(Moe1Args a, hipStream_t st) {
 template <int FMT>
 moe_status launch_moe1_fmt(const Moe1Args& a, hipStream_t st) {
   // SGU = I*k / (kG1 * 32), SDN = ceil(H*k / (kG1 * 32))
+  if (a.xr) {
+    // latent layers (router on the hidden state): the latent K3 and W50 shapes
+    if (a.H == 3584 && a.I == 3072 && a.k == 16) return launch_moe1_kernel<FMT, 7, 6, 6, 7, 16, true>(a, st);
+    if (a.H == 3584 && a.I == 3072 && a.k == 8) return launch_moe1_kernel<FMT, 7, 6, 3, 4, 8, true>(a, st);
+    return MOE_ERR_UNSUPPORTED;
+  }
   if (a.H == 7168 && a.I == 1536 && a.k == 16) return launch_moe1_kernel<FMT, 14, 3, 3, 14, 16>(a, st);
   if (a.H == 3584 && a.I == 3072 && a.k == 16) return launch_moe1_kernel<FMT, 7, 6, 6, 7, 16>(a, st);
   if (a.H == 3584 && a.I == 3072 && a.k == 8) return launch_moe1_kernel<FMT, 7, 6, 3, 4, 8>(a, st);
@@ -1608,13 +1634,16 @@ bool moe1_fits(const moe_bank* b, int C, int k) {
 // that case.
 moe_status launch_moe1(const moe_bank* b, const float* Wr, const float* x, int k,
                        const int32_t* idx_in, const float* w_in, int32_t* idx_out, float* w_out,
-                       float* out, uint8_t* ws, const WsLayout& L, hipStream_t st) {
+                       float* out, uint8_t* ws, const WsLayout& L, hipStream_t st,
+                       const float* xr = nullptr, int Hr = 0) {
   Moe1Args a;
   a.base = static_cast<const uint8_t*>(b->base);
   a.stride = b->expert_stride;
   for (int t = 0; t < MOE_NUM_TENSORS; ++t) a.off[t] = b->offset[t];
   a.E = b->num_experts; a.H = b->hidden; a.I = b->inter; a.k = k;
-  a.x = x; a.Wr = Wr; a.idx_in = idx_in; a.w_in = w_in; a.idx_out = idx_out; a.w_out = w_out;
+  a.x = x; a.Wr = Wr;
+  a.xr = xr;             // null: the router reads x
+  a.Hr = xr ? Hr : 0; a.idx_in = idx_in; a.w_in = w_in; a.idx_out = idx_out; a.w_out = w_out;
   a.tlogits = reinterpret_cast<uint64_t*>(ws + L.tlogits);
   a.th = reinterpret_cast<uint64_t*>(ws + L.th);
   a.tpart = reinterpret_cast<uint64_t*>(ws + L.tpart);
@@ -1630,6 +1659,23 @@ bool batched_shape(const moe_bank* b) { return batched_shape_ok(b); }
 bool topk_ok(int k, int E) { return k >= 1 && k <= MOE_MAX_TOPK && k <= E; }
 
 }  // namespace
+
+namespace rf4 {
+moe_status layer1_router_input(const moe_bank* b, const float* w_router, const float* xr, int Hr,
+                               const float* x, int k, float* out, int32_t* idx, float* w,
+                               void* ws, size_t ws_bytes, hipStream_t st) {
+  if (check_bank(b) != MOE_OK || !moe1_fits(b, 1, k) || !topk_ok(k, b->num_experts))
+    return MOE_ERR_UNSUPPORTED;
+  if (Hr < 32 || Hr % 32 || Hr > kMaxH1) return MOE_ERR_UNSUPPORTED;
+  if (!w_router || !xr || !x || !out || !idx || !w || !aligned(xr, 16) || !aligned(x, 16) ||
+      !aligned(w_router, 16))
+    return MOE_ERR_INVALID_ARG;
+  const WsLayout L = ws_layout(b->num_experts, b->hidden, b->inter, k, 1);
+  if (!ws || ws_bytes < L.total || !aligned(ws, 256)) return MOE_ERR_WORKSPACE;
+  return launch_moe1(b, w_router, x, k, nullptr, nullptr, idx, w, out, static_cast<uint8_t*>(ws), L,
+                     st, xr, Hr);
+}
+}  // namespace rf4
 
 // ===========================================================================
 // C ABI
