@@ -43,7 +43,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="k3_stack",
                    choices=["k3_stack", "k3_stack_zipf", "w50_k16", "w50_k8", "w50_c7_k8",
-                            "w50_c7_k16", "tiny", "k3_prefill", "k3_latent"],
+                            "w50_c7_k16", "tiny", "k3_prefill", "w50_prefill", "k3_latent"],
                    help="k3_stack (the headline: 12 layers, uniform routing), k3_stack_zipf "
                         "(Zipf s=1.2), one of the single-layer decode workloads, or k3_latent "
                         "(whole latent layers: router, routed_down, routed experts, norm, "
@@ -57,6 +57,10 @@ def parse():
     p.add_argument("--layer-only", action="store_true",
                    help="time only the whole-layer step (no expert-only / route-only loops), "
                         "so a kernel trace holds only the layer kernel's launches")
+    p.add_argument("--mx-mma", type=int, default=0, metavar="T",
+                   help="MXFP4 workloads: run the experts on the block-scaled FP4 matrix cores "
+                        "with T activation terms (moe_route + moe_expert_fwd_mx_mma per layer "
+                        "call) instead of moe_layer_fwd")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run a plain 2 GiB device copy (HBM counter calibration)")
     return p.parse_args()
@@ -354,6 +358,20 @@ def main():
         for l in range(wl.layers):
             rf.moe_layer_fwd(banks[l], wrs[l], xs[l][j * C:(j + 1) * C], C, wl.k, outs[l], ws=ws)
 
+    if args.mx_mma:
+        if wl.fmt != synth.FMT_MX:
+            raise SystemExit("--mx-mma needs an MXFP4 workload")
+        mws = rf.MxMmaWorkspace(banks[0], wl.k, C, args.mx_mma, device=dev)
+        ridx = torch.empty((C, wl.k), dtype=torch.int32, device=dev)
+        rw = torch.empty((C, wl.k), dtype=torch.float32, device=dev)
+
+        def step(i):  # noqa: F811  (the same step with the experts on the FP4 matrix cores)
+            j = i % pool
+            for l in range(wl.layers):
+                xj = xs[l][j * C:(j + 1) * C]
+                rf.moe_route(xj, wrs[l], None, C, wl.H, wl.E, wl.k, ridx, rw, ws)
+                rf.moe_expert_fwd_mx_mma(banks[l], xj, C, wl.k, ridx, rw, outs[l], args.mx_mma, mws)
+
     # ---- whole path ----
     for i in range(args.warmup):
         step(i)
@@ -420,7 +438,11 @@ def main():
     alg_bytes = router_bytes + sel_bytes + 2 * C * wl.H * 4
     gbps_kernel = alg_bytes / (us_call * 1e-6) / 1e9
     fmt = "nvfp4" if wl.fmt == synth.FMT_NV else "mxfp4"
-    if C == 1 and wl.name != "tiny":
+    if args.mx_mma:
+        kernel = (f"k_brouter + k_btopk, then k_mq_split + k_mcount/k_mscan/k_mscatter + "
+                  f"k_mgemm<GU> + k_mq_split + k_mgemm<DN> + k_mcombine ({args.mx_mma} e4m3 "
+                  "activation terms) per layer call")
+    elif C == 1 and wl.name != "tiny":
         kernel = "k_moe1 (whole layer, one launch per moe_layer_fwd call)"
     elif wl.name == "tiny":
         kernel = "k_route + k_btopk + k_gate_up + k_down (+ k_zero_uncovered) per moe_layer_fwd call"

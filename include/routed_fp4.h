@@ -214,6 +214,28 @@ moe_status moe_latent_layer_fwd(const moe_latent_layer *layer, const float *x, i
                                 int32_t k, float *out, int32_t *topk_idx_out, float *topk_w_out,
                                 void *ws, size_t ws_bytes, void *stream);
 
+/* MXFP4 experts on the block-scaled FP4 matrix cores (page "SparkInfer-K3",
+ * section "Where to customize": without FP4 tensor cores every low-bit expert
+ * product dequantises to bf16 first; CDNA4's v_mfma_scale_f32_16x16x128_f8f6f4
+ * takes the MXFP4 codes and their e8m0 block scales as they are stored).
+ * The same computation as moe_expert_fwd for an MXFP4 bank: the fp32
+ * activations (x, and h after SwiGLU) enter as `terms` e4m3 terms with an
+ * e8m0 scale per 32 values; terms = 1 is a lossy single-term mode, and each
+ * further term takes about 4 more bits.  The instruction adds each group of
+ * 8 products in fixed point about 13 bits below the group's largest
+ * (measured), so the error levels off near 2e-5 rel-L2 from terms = 4 on:
+ * a near-exact mode, not bit-for-bit the fp32 path.
+ *  bank: MXFP4, hidden and inter multiples of 256.  1 <= C <= MOE_MAX_TOKENS,
+ *  1 <= k <= min(E, MOE_MAX_TOPK), 1 <= terms <= 6.  x [C][H] and out [C][H]
+ *  fp32, 16-byte aligned, not aliased; topk_idx / topk_w [C][k] (an
+ *  out-of-range expert index contributes zero).  The workspace (256-byte
+ *  aligned) needs no initialisation.  Returns MOE_ERR_UNSUPPORTED outside
+ *  these limits (including NVFP4 banks). */
+size_t moe_mx_mma_workspace_size(const moe_bank *bank, int32_t top_k, int32_t C, int32_t terms);
+moe_status moe_expert_fwd_mx_mma(const moe_bank *bank, const float *x, int32_t C, int32_t k,
+                                 const int32_t *topk_idx, const float *topk_w, float *out,
+                                 int32_t terms, void *ws, size_t ws_bytes, void *stream);
+
 /* Test export: dequantise one matrix of one expert to fp32.
  *  matrix 0 = gate [I][H], 1 = up [I][H], 2 = down [H][I].
  *  MXFP4: w = e2m1 * 2^(b-127), exact (IEEE denormals kept).

@@ -26,7 +26,8 @@ BLOCK = {MOE_FMT_MXFP4: 32, MOE_FMT_NVFP4: 16}
 
 EXPORTS = ("moe_version", "moe_status_string", "moe_bank_layout", "moe_workspace_size",
            "moe_workspace_init", "moe_route", "moe_expert_fwd", "moe_layer_fwd", "moe_dequant",
-           "moe_latent_workspace_size", "moe_latent_layer_fwd")
+           "moe_latent_workspace_size", "moe_latent_layer_fwd", "moe_mx_mma_workspace_size",
+           "moe_expert_fwd_mx_mma")
 
 
 class MoeError(RuntimeError):
@@ -73,6 +74,8 @@ def lib() -> ctypes.CDLL:
             "moe_dequant": ([P, i32, i32, P, P], i32),
             "moe_latent_workspace_size": ([P, i32, i32], sz),
             "moe_latent_layer_fwd": ([P, P, i32, i32, P, P, P, P, sz, P], i32),
+            "moe_mx_mma_workspace_size": ([P, i32, i32, i32], sz),
+            "moe_expert_fwd_mx_mma": ([P, P, i32, i32, P, P, P, i32, P, sz, P], i32),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -272,3 +275,33 @@ def moe_latent_layer_fwd(layer: LatentLayer, x, C, k, out, topk_idx_out=None, to
         _ptr(out, torch.float32, (C, H), "out"),
         _ptr(topk_idx_out, torch.int32, (C, k), "topk_idx_out"),
         _ptr(topk_w_out, torch.float32, (C, k), "topk_w_out"), ws.ptr, ws.nbytes, _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+# MXFP4 experts on the block-scaled FP4 matrix cores
+# ---------------------------------------------------------------------------
+class MxMmaWorkspace:
+    def __init__(self, bank: Bank, top_k: int, C: int, terms: int, device="cuda"):
+        import torch
+        n = lib().moe_mx_mma_workspace_size(_bank(bank), top_k, C, terms)
+        if n == 0:
+            raise MoeError("moe_mx_mma_workspace_size", MOE_ERR_UNSUPPORTED)
+        self.tensor = torch.empty((n + 255) // 256 * 256 // 4, dtype=torch.int32, device=device)
+
+    @property
+    def ptr(self):
+        return ctypes.c_void_p(self.tensor.data_ptr())
+
+    @property
+    def nbytes(self):
+        return self.tensor.numel() * 4
+
+
+def moe_expert_fwd_mx_mma(bank: Bank, x, C, k, topk_idx, topk_w, out, terms: int,
+                          ws: MxMmaWorkspace, stream=None):
+    import torch
+    H = bank.H
+    _check("moe_expert_fwd_mx_mma", lib().moe_expert_fwd_mx_mma(
+        _bank(bank), _ptr(x, torch.float32, (C, H), "x"), C, k,
+        _ptr(topk_idx, torch.int32, (C, k), "topk_idx"), _ptr(topk_w, torch.float32, (C, k), "topk_w"),
+        _ptr(out, torch.float32, (C, H), "out"), terms, ws.ptr, ws.nbytes, _stream(stream)))

@@ -260,6 +260,9 @@ WORKLOADS = {
     "k3_stack": Workload("k3_stack", FMT_NV, 896, 16, 7168, 1536, 1, 12),
     "k3_stack_zipf": Workload("k3_stack_zipf", FMT_NV, 896, 16, 7168, 1536, 1, 12, "zipf", 1.2),
     "k3_prefill": Workload("k3_prefill", FMT_NV, 896, 16, 7168, 1536, 2048, 1, "zipf", 1.0, True),
+    # a 2048-token chunk through one MXFP4 layer of the W50 shape (the format the
+    # block-scaled FP4 matrix cores take as stored)
+    "w50_prefill": Workload("w50_prefill", FMT_MX, 448, 8, 3584, 3072, 2048, 1, "zipf", 1.0, True),
 }
 
 
