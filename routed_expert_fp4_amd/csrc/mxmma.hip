@@ -50,7 +50,7 @@ typedef float v4f_t __attribute__((ext_vector_type(4)));
 constexpr int kMTile = 64;      // pairs per tile (4 column tiles of 16)
 constexpr int kMRows = 256;     // the row blocks divide H and I
 // row tiles of 16 per wave: gate/up holds two matrices' accumulators
-template <bool GU> constexpr int mrt() { return GU ? 2 : 4; }
+template <bool GU> constexpr int mrt() { return GU ? 1 : 2; }
 
 struct MArgs {
   const uint8_t* base;
@@ -214,15 +214,17 @@ __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + expf(-z));
 
 // One tile (expert e, up to 64 pairs) against 64 RT weight rows (RT = 2 for
 // gate/up, whose two matrices double the accumulators, 4 for down): wave w
-// takes rows 16 RT w .. 16 RT w + 16 RT - 1 as RT row tiles of 16, for every 16-pair
-// column tile of the tile and every term.  Per K step of 128: one 16-byte
-// code load and one scale byte per row tile and matrix (straight from HBM, no
-// conversion), and two 16-byte term loads and one scale byte per column tile
-// and term (from L2: every tile of an expert reads the same activations).
+// takes rows 16 RT w .. 16 RT w + 16 RT - 1 as RT row tiles of 16, for every
+// 16-pair column tile of the tile and every term.  Per K step of 128: one
+// 16-byte code load and one scale byte per row tile and matrix (straight from
+// HBM, no conversion); per stage (K step, term) the tile's activation
+// fragments once for the workgroup, through LDS.
 template <bool GU>
-__global__ __launch_bounds__(256) void k_mgemm(MArgs a) {
+__global__ __launch_bounds__(256, 2) void k_mgemm(MArgs a) {
   constexpr int NM = GU ? 2 : 1, RT = mrt<GU>();
   __shared__ int s_pair[kMTile], s_row[kMTile];
+  __shared__ __attribute__((aligned(16))) uint8_t s_b[2][kMTile][144];   // 128 bytes + pad per pair
+  __shared__ uint32_t s_bs[2][kMTile];
   const int tile = blockIdx.y;
   if (tile >= (int)a.meta[0]) return;
   const int e = a.tiles[2 * tile], first = a.tiles[2 * tile + 1];
@@ -253,9 +255,6 @@ __global__ __launch_bounds__(256) void k_mgemm(MArgs a) {
   }
   const int nrow0 = (blockIdx.x * 4 + wave) * 16 * RT;
   const int nsub = (cnt + 15) / 16;
-  int arow[4];
-#pragma unroll
-  for (int sb = 0; sb < 4; ++sb) arow[sb] = s_row[16 * sb + c16];
 
   v4f_t acc[RT][NM][4];
 #pragma unroll
@@ -265,61 +264,82 @@ __global__ __launch_bounds__(256) void k_mgemm(MArgs a) {
 #pragma unroll
       for (int sb = 0; sb < 4; ++sb) acc[rt][m][sb] = v4f_t{0.f, 0.f, 0.f, 0.f};
 
-  // weights one K step ahead in registers; each step's activation fragments
-  // (all column tiles of one term) are loaded before their MFMAs
-  v8i_t av[RT][NM], an[RT][NM];
-  int as[RT][NM], asn[RT][NM];
-  auto load_a = [&](int k0, v8i_t (&dst)[RT][NM], int (&ds)[RT][NM]) {
+  // Stages (K step, term), in order.  A stage's activation fragments for
+  // the whole tile (64 pairs x 128 bytes + 4 scale bytes each) are loaded
+  // once per workgroup, one stage ahead, into registers and then into a
+  // double-buffered LDS tile that the four waves read.  The weights of even
+  // and odd K steps sit in two register sets (A0, A1), each reloaded for the
+  // step after next as soon as its own step's MFMAs are issued, so no copies
+  // between them make a load wait.
+  v8i_t A0[RT][NM], A1[RT][NM];
+  int S0[RT][NM], S1[RT][NM];
+  auto load_a = [&](int k0, v8i_t (&A)[RT][NM], int (&S)[RT][NM]) {
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       const size_t row = (size_t)(nrow0 + 16 * rt + c16);
 #pragma unroll
       for (int m = 0; m < NM; ++m) {
         const uint4 c = *reinterpret_cast<const uint4*>(cb[m] + row * (K / 2) + k0 / 2 + 16 * g);
-        dst[rt][m] = v8i_t{(int)c.x, (int)c.y, (int)c.z, (int)c.w, 0, 0, 0, 0};
-        ds[rt][m] = sbp[m][row * KB + k0 / 32 + g];
+        A[rt][m] = v8i_t{(int)c.x, (int)c.y, (int)c.z, (int)c.w, 0, 0, 0, 0};
+        S[rt][m] = sbp[m][row * KB + k0 / 32 + g];
       }
     }
   };
-  load_a(0, an, asn);
-  for (int k0 = 0; k0 < K; k0 += 128) {
+  const int lp = tid >> 2, lc = tid & 3;            // loader: pair, 32-byte chunk
+  const int lrow = s_row[lp];
+  uint4 g0, g1;
+  uint32_t gsc = 0u;
+  auto gload = [&](int k0, int t) {
+    const size_t qrow = (size_t)t * R + lrow;
+    const uint8_t* qp = q + qrow * K + k0 + 32 * lc;
+    g0 = *reinterpret_cast<const uint4*>(qp);
+    g1 = *reinterpret_cast<const uint4*>(qp + 16);
+    gsc = *reinterpret_cast<const uint32_t*>(qs + qrow * KB + k0 / 32);   // all lanes: no branch
+  };
+  auto sstore = [&](int buf) {
+    *reinterpret_cast<uint4*>(&s_b[buf][lp][32 * lc]) = g0;
+    *reinterpret_cast<uint4*>(&s_b[buf][lp][32 * lc + 16]) = g1;
+    if (lc == 0) s_bs[buf][lp] = gsc;
+  };
+  const int T = a.T;
+  int buf = 0;
+  // the T stages of K step k0 with weights A / S
+  auto run_step = [&](int k0, const v8i_t (&A)[RT][NM], const int (&S)[RT][NM]) {
+    for (int t = 0; t < T; ++t) {
+      const bool more = t + 1 < T || k0 + 128 < K;
+      if (more) gload(t + 1 < T ? k0 : k0 + 128, t + 1 < T ? t + 1 : 0);
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
+      for (int sb = 0; sb < 4; ++sb) {
+        if (sb < nsub) {
+          const int pr = 16 * sb + c16;
+          const uint4 b0 = *reinterpret_cast<const uint4*>(&s_b[buf][pr][16 * g]);
+          const uint4 b1 = *reinterpret_cast<const uint4*>(&s_b[buf][pr][64 + 16 * g]);
+          const v8i_t bv = v8i_t{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w,
+                                 (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+          const int bsc = (int)((s_bs[buf][pr] >> (8 * g)) & 0xFFu);
 #pragma unroll
-      for (int m = 0; m < NM; ++m) { av[rt][m] = an[rt][m]; as[rt][m] = asn[rt][m]; }
-    if (k0 + 128 < K) load_a(k0 + 128, an, asn);
-    constexpr int TB = 1;                 // terms per batch of fragment loads
-    for (int t0 = 0; t0 < a.T; t0 += TB) {
-      v8i_t bv[4][TB];
-      int bs[4][TB];
+          for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-      for (int sb = 0; sb < 4; ++sb)
-#pragma unroll
-        for (int u = 0; u < TB; ++u) {
-          if (sb < nsub && t0 + u < a.T) {
-            const size_t qrow = (size_t)(t0 + u) * R + arow[sb];
-            const uint8_t* qp = q + qrow * K + k0 + 16 * g;
-            const uint4 b0 = *reinterpret_cast<const uint4*>(qp);
-            const uint4 b1 = *reinterpret_cast<const uint4*>(qp + 64);
-            bv[sb][u] = v8i_t{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w,
-                              (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
-            bs[sb][u] = qs[qrow * KB + k0 / 32 + g];
-          }
+            for (int m = 0; m < NM; ++m)
+              acc[rt][m][sb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                  A[rt][m], bv, acc[rt][m][sb], 4, 0, 0, S[rt][m], 0, bsc);
         }
-#pragma unroll
-      for (int sb = 0; sb < 4; ++sb)
-#pragma unroll
-        for (int u = 0; u < TB; ++u) {
-          if (sb < nsub && t0 + u < a.T) {
-#pragma unroll
-            for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-              for (int m = 0; m < NM; ++m)
-                acc[rt][m][sb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                    av[rt][m], bv[sb][u], acc[rt][m][sb], 4, 0, 0, as[rt][m], 0, bs[sb][u]);
-          }
-        }
+      }
+      if (more) sstore(buf ^ 1);
+      __syncthreads();
+      buf ^= 1;
     }
+  };
+  load_a(0, A0, S0);
+  load_a(128, A1, S1);                               // K is a multiple of 256
+  gload(0, 0);
+  sstore(0);
+  __syncthreads();
+  for (int k0 = 0; k0 < K; k0 += 256) {
+    run_step(k0, A0, S0);
+    if (k0 + 256 < K) load_a(k0 + 256, A0, S0);
+    run_step(k0 + 128, A1, S1);
+    if (k0 + 384 < K) load_a(k0 + 384, A1, S1);
   }
 
 #pragma unroll
