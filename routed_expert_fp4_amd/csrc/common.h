@@ -337,5 +337,8 @@ moe_status launch_batched_decode(const moe_bank* b, const float* x, int C, int k
 moe_status layer1_router_input(const moe_bank* b, const float* w_router, const float* xr, int Hr,
                                const float* x, int k, float* out, int32_t* idx, float* w,
                                void* ws, size_t ws_bytes, hipStream_t st);
+// bank_status: the checks every expert entry point makes of a bank (format,
+// sizes, alignment, tensor offsets within the stride).
+moe_status bank_status(const moe_bank* b);
 
 }  // namespace rf4

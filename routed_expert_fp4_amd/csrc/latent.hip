@@ -37,6 +37,7 @@ struct GemvArgs {
   int accumulate;         // 1: y += result
   int32_t* sel_idx;       // or null: [C][ns] shared-expert selection to write
   float* sel_w;
+  int32_t* sel_disp;      // or null: the shared experts' dispatch table to write
   int ns;
 };
 
@@ -79,9 +80,23 @@ __global__ __launch_bounds__(kGemvWG) void k_gemv(GemvArgs a) {
   const bool norm = a.gamma != nullptr;
 
   if (a.sel_idx && blockIdx.x == 0) {
-    for (int i = tid; i < C * a.ns; i += kGemvWG) {
-      a.sel_idx[i] = i % a.ns;
+    const int ns = a.ns, CK = C * ns;
+    for (int i = tid; i < CK; i += kGemvWG) {
+      a.sel_idx[i] = i % ns;
       a.sel_w[i] = 1.0f;
+    }
+    if (a.sel_disp) {
+      // distinct experts in order of first use (0 .. ns-1), each with every
+      // token's pair t * ns + u in token order
+      if (tid == 0) a.sel_disp[0] = ns;
+      for (int u = tid; u < ns; u += kGemvWG) {
+        a.sel_disp[disp_uexp(CK) + u] = u;
+        a.sel_disp[disp_untok(CK) + u] = C;
+      }
+      for (int i = tid; i < CK; i += kGemvWG) {
+        const int u = i / C, t = i - u * C;
+        a.sel_disp[disp_upair(CK) + u * C + t] = t * ns + u;
+      }
     }
   }
 
@@ -281,6 +296,11 @@ moe_status moe_latent_layer_fwd(const moe_latent_layer* layer, const float* x, i
   g.W = layer->w_down; g.x = x; g.gamma = nullptr; g.eps = 0.0f; g.y = xlat;
   g.C = C; g.N = L; g.K = H; g.accumulate = 0;
   g.sel_idx = sidx; g.sel_w = sw; g.ns = ns;     // the shared experts' selection
+  // and, where the decode-batch streams take the shared bank, its dispatch
+  // table (every token, every shared expert), so no dispatch launch is needed
+  const bool shared_streams = bank_status(&S) == MOE_OK && batched_decode_shape(&S, C);
+  const WsLayout Ls = ws_layout(ns, S.hidden, S.inter, ns, C);
+  g.sel_disp = shared_streams ? reinterpret_cast<int32_t*>(w8 + W.shared + Ls.disp) : nullptr;
   moe_status s = launch_gemv(g, st);
   if (s != MOE_OK) return s;
   s = C == 1 ? layer1_router_input(&R, layer->w_router, x, H, xlat, k, ylat, idx, w, wr, wr_bytes, st)
@@ -293,11 +313,13 @@ moe_status moe_latent_layer_fwd(const moe_latent_layer* layer, const float* x, i
   }
   if (s != MOE_OK) return s;
   // finish phase: shared experts into out, then routed_norm and routed_up added
-  s = moe_expert_fwd(&S, x, C, ns, sidx, sw, out, w8 + W.shared, ws_bytes_s, stream);
+  s = shared_streams
+          ? launch_batched_decode(&S, x, C, ns, sidx, sw, out, w8 + W.shared, Ls, st)
+          : moe_expert_fwd(&S, x, C, ns, sidx, sw, out, w8 + W.shared, ws_bytes_s, stream);
   if (s != MOE_OK) return s;
   g.W = layer->w_up; g.x = ylat; g.gamma = layer->norm_gamma; g.eps = layer->norm_eps; g.y = out;
   g.C = C; g.N = H; g.K = L; g.accumulate = 1;
-  g.sel_idx = nullptr; g.sel_w = nullptr; g.ns = 0;
+  g.sel_idx = nullptr; g.sel_w = nullptr; g.sel_disp = nullptr; g.ns = 0;
   return launch_gemv(g, st);
 }
 

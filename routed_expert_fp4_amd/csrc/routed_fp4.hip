@@ -1675,6 +1675,7 @@ moe_status layer1_router_input(const moe_bank* b, const float* w_router, const f
   return launch_moe1(b, w_router, x, k, nullptr, nullptr, idx, w, out, static_cast<uint8_t*>(ws), L,
                      st, xr, Hr);
 }
+moe_status bank_status(const moe_bank* b) { return check_bank(b); }
 }  // namespace rf4
 
 // ===========================================================================
