@@ -121,3 +121,79 @@ def test_route_and_expert_fwd_reject_bad_arguments(rf):
     assert L.moe_dequant(ctypes.byref(b), 8, 0, FAKE, None) == rf.MOE_ERR_INVALID_ARG
     assert L.moe_dequant(ctypes.byref(b), 0, 3, FAKE, None) == rf.MOE_ERR_INVALID_ARG
     assert L.moe_workspace_init(None, 16, None) == rf.MOE_ERR_INVALID_ARG
+
+
+def _mx_bank(rf, fmt=None, H=512, I=768, E=16):
+    fmt = rf.MOE_FMT_MXFP4 if fmt is None else fmt
+    off, stride = rf.moe_bank_layout(fmt, H, I)
+    return rf.moe_bank(fmt, E, H, I, 0x100000, stride, (ctypes.c_int64 * 7)(*off))
+
+
+def test_mx_mma_limits_and_rejections(rf):
+    """Workspace sizing is pure host arithmetic; every rejected call returns
+    before anything is enqueued."""
+    L = rf.lib()
+    b = _mx_bank(rf)
+    size = L.moe_mx_mma_workspace_size(ctypes.byref(b), 4, 24, 2)
+    assert size > 24 * 512 * 2                                   # at least x's two terms
+    assert L.moe_mx_mma_workspace_size(ctypes.byref(b), 4, 24, 0) == 0
+    assert L.moe_mx_mma_workspace_size(ctypes.byref(b), 4, 24, 7) == 0
+    assert L.moe_mx_mma_workspace_size(ctypes.byref(b), 17, 24, 2) == 0       # k > E
+    assert L.moe_mx_mma_workspace_size(ctypes.byref(b), 4, 0, 2) == 0
+    assert L.moe_mx_mma_workspace_size(ctypes.byref(_mx_bank(rf, rf.MOE_FMT_NVFP4)), 4, 24, 2) == 0
+    assert L.moe_mx_mma_workspace_size(ctypes.byref(_mx_bank(rf, H=384)), 4, 24, 2) == 0
+    assert L.moe_mx_mma_workspace_size(None, 4, 24, 2) == 0
+    out = ctypes.c_void_p(0x30000)
+    ws = ctypes.c_void_p(0x400000)
+
+    def call(bank=b, x=FAKE, o=out, ws=ws, n=size, terms=2, idx=FAKE):
+        return L.moe_expert_fwd_mx_mma(ctypes.byref(bank) if bank is not None else None, x, 24, 4,
+                                       idx, FAKE, o, terms, ws, n, None)
+
+    assert call(bank=None) == rf.MOE_ERR_INVALID_ARG
+    assert call(x=None) == rf.MOE_ERR_INVALID_ARG
+    assert call(idx=None) == rf.MOE_ERR_INVALID_ARG
+    assert call(o=FAKE) == rf.MOE_ERR_INVALID_ARG                           # out aliases x
+    assert call(x=ctypes.c_void_p(0x20004)) == rf.MOE_ERR_INVALID_ARG       # misaligned x
+    assert call(bank=_mx_bank(rf, rf.MOE_FMT_NVFP4)) == rf.MOE_ERR_UNSUPPORTED
+    assert call(terms=0) == rf.MOE_ERR_UNSUPPORTED
+    assert call(ws=None) == rf.MOE_ERR_WORKSPACE
+    assert call(n=size - 1) == rf.MOE_ERR_WORKSPACE
+    assert call(ws=ctypes.c_void_p(0x400010)) == rf.MOE_ERR_WORKSPACE       # misaligned workspace
+
+
+def test_latent_limits_and_rejections(rf):
+    L = rf.lib()
+    routed = _mx_bank(rf, rf.MOE_FMT_NVFP4, H=512, I=512, E=64)
+    shared = _mx_bank(rf, rf.MOE_FMT_NVFP4, H=1024, I=1024, E=2)
+
+    def layer(**kw):
+        lay = rf.moe_latent_layer(1024, 0x20000, 0x40000, 0x50000, 1e-6, 0x60000, routed, shared)
+        for k, v in kw.items():
+            setattr(lay, k, v)
+        return lay
+
+    good = layer()
+    size = L.moe_latent_workspace_size(ctypes.byref(good), 8, 4)
+    assert size > 0
+    assert L.moe_latent_workspace_size(None, 8, 4) == 0
+    assert L.moe_latent_workspace_size(ctypes.byref(good), 8, 17) == 0       # C above the decode limit
+    assert L.moe_latent_workspace_size(ctypes.byref(good), 65, 4) == 0       # k > E
+    assert L.moe_latent_workspace_size(ctypes.byref(layer(w_down=None)), 8, 4) == 0
+    assert L.moe_latent_workspace_size(ctypes.byref(layer(norm_eps=-1.0)), 8, 4) == 0
+    assert L.moe_latent_workspace_size(ctypes.byref(layer(hidden=2048)), 8, 4) == 0   # shared bank width
+    out = ctypes.c_void_p(0x30000)
+    ws = ctypes.c_void_p(0x400000)
+
+    def call(lay=good, x=ctypes.c_void_p(0x70000), o=out, C=4, ws=ws, n=size):
+        return L.moe_latent_layer_fwd(ctypes.byref(lay) if lay is not None else None, x, C, 8, o,
+                                      None, None, ws, n, None)
+
+    assert call(lay=None) == rf.MOE_ERR_INVALID_ARG
+    assert call(x=None) == rf.MOE_ERR_INVALID_ARG
+    assert call(o=ctypes.c_void_p(0x70000)) == rf.MOE_ERR_INVALID_ARG       # out aliases x
+    assert call(C=17) == rf.MOE_ERR_UNSUPPORTED
+    assert call(ws=None) == rf.MOE_ERR_WORKSPACE
+    assert call(n=size - 1) == rf.MOE_ERR_WORKSPACE
+    assert call(x=ctypes.c_void_p(0x70004)) == rf.MOE_ERR_INVALID_ARG       # misaligned x
+    assert call(lay=layer(w_up=0x60008)) == rf.MOE_ERR_INVALID_ARG          # misaligned routed_up
