@@ -143,3 +143,29 @@ def test_mx_mma_repeat_bit_identical():
     a, *_ = _run(wl, 4)
     b, *_ = _run(wl, 4)
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+@pytest.mark.parametrize("terms", [4, 1])
+def test_mx_mma_w50_prefill_full_size_sampled(terms):
+    """The bench's FP4 matrix-core configuration at full size: one 2048-token
+    bf16-exact chunk through the W50 MXFP4 layer (448 experts, top-8, Zipf
+    1.0); token 0, the first and last tokens of the most loaded expert, and
+    the last token against the oracle.  Four terms: the instruction's floor;
+    one term: the lossy mode's bound."""
+    wl = synth.WORKLOADS["w50_prefill"]
+    say(f"[mx mma] W50 prefill chunk C={wl.C} terms={terms}")
+    got, x, idx, w, spec = _run(wl, terms)
+    counts = np.bincount(idx.ravel(), minlength=wl.E)
+    hot = int(np.argmax(counts))
+    say(f"  hottest expert {hot} with {counts.max()} pairs, {int((counts > 0).sum())} experts touched")
+    assert counts.max() > 64                      # several 64-pair tiles for one expert
+    hot_tokens = np.nonzero((idx == hot).any(axis=1))[0]
+    cache = {}
+    for t in sorted({0, int(hot_tokens[0]), int(hot_tokens[-1]), wl.C - 1}):
+        ref = oracle.experts_forward(spec, x[[t]], idx[[t]], w[[t]], cache)
+        if terms >= 4:
+            assert_floor(got[[t]], ref, f"W50 prefill token {t}")
+        else:
+            r = oracle.rel_l2(got[[t]], ref)
+            say(f"  W50 prefill token {t} (1 term): rel_l2 {r:.3e}")
+            assert r < 0.1
