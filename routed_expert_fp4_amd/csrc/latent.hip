@@ -22,6 +22,9 @@
 //               1 / rms(x[t]), else s_t = 1 and g = 1.  The routed_down launch
 //               also writes the shared experts' selection (every token, every
 //               shared expert, weight 1).
+//   k_sgu, k_sdn the shared experts for one token: gate/up with SwiGLU, then
+//               down summed over the shared experts, as row-blocked mat-vecs
+//               (more tokens take the library's decode-batch streams)
 #include "common.h"
 
 namespace rf4 {
@@ -211,6 +214,213 @@ moe_status launch_gemv(const GemvArgs& a, hipStream_t st) {
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_DEVICE;
 }
 
+// ---------------------------------------------------------------------------
+// Shared experts for one token: every shared expert, weight 1, as two
+// row-blocked mat-vec launches (the decode-batch streams, built for many
+// experts, leave most CUs idle on two).
+// ---------------------------------------------------------------------------
+struct SArgs {
+  const uint8_t* base;
+  int64_t stride;
+  int64_t off[MOE_NUM_TENSORS];
+  int ns, H, I;
+  const float* x;   // [H]
+  float* h;         // [ns][I]
+  float* out;       // [H]
+};
+
+constexpr int kSRowsGU = 4;      // intermediate rows (gate and up) per workgroup
+constexpr int kSRowsDN = 8;      // output rows per workgroup
+constexpr int kSMaxCh = 2;       // 32-element chunks per thread (K <= 16384)
+
+// sum over one 32-element chunk of w * x: MXFP4 with the power-of-two scale
+// applied in the conversion, NVFP4 as two 16-element block sums times their
+// e4m3 scales (the tensor's global scale is applied by the caller)
+template <int FMT>
+__device__ __forceinline__ float sdot32(const uint4& q, uint32_t sc, const float* xv) {
+  constexpr bool MX = FMT == MOE_FMT_MXFP4;
+  const float s = MX ? __uint_as_float((sc & 0xFFu) << 23) : 1.0f;
+  float b[2] = {0.0f, 0.0f};
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const uint32_t wd = d == 0 ? q.x : d == 1 ? q.y : d == 2 ? q.z : q.w;
+    const auto v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd, s, 0);
+    const auto v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd, s, 1);
+    const auto v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd, s, 2);
+    const auto v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd, s, 3);
+    float t = b[d >> 1];
+    t += v0[0] * xv[8 * d + 0]; t += v0[1] * xv[8 * d + 1];
+    t += v1[0] * xv[8 * d + 2]; t += v1[1] * xv[8 * d + 3];
+    t += v2[0] * xv[8 * d + 4]; t += v2[1] * xv[8 * d + 5];
+    t += v3[0] * xv[8 * d + 6]; t += v3[1] * xv[8 * d + 7];
+    b[d >> 1] = t;
+  }
+  if (MX) return b[0] + b[1];
+  return b[0] * __builtin_amdgcn_cvt_f32_fp8((int)sc, 0) + b[1] * __builtin_amdgcn_cvt_f32_fp8((int)sc, 1);
+}
+
+template <int FMT>
+__device__ __forceinline__ uint32_t sscale(const uint8_t* srow, int c) {
+  if (FMT == MOE_FMT_MXFP4) return srow[c];
+  return *reinterpret_cast<const uint16_t*>(srow + 2 * c);
+}
+
+// gate and up rows i0 .. i0+3 of shared expert blockIdx.y: the 256 threads
+// split K into 32-element chunks (x in registers), every weight load is
+// issued first, sums are reduced over the wave (DPP) and the four waves in
+// order; h = silu(g) * u.
+template <int FMT>
+__global__ __launch_bounds__(256) void k_sgu(SArgs a) {
+  constexpr int B = FMT == MOE_FMT_MXFP4 ? 32 : 16;
+  __shared__ float s_part[4][2 * kSRowsGU];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int j = blockIdx.y, i0 = blockIdx.x * kSRowsGU, H = a.H, nch = H / 32;
+  const uint8_t* rec = a.base + (size_t)j * a.stride;
+  const uint8_t* cb[2] = {rec + a.off[MOE_T_GATE_CODES], rec + a.off[MOE_T_UP_CODES]};
+  const uint8_t* sbp[2] = {rec + a.off[MOE_T_GATE_SCALES], rec + a.off[MOE_T_UP_SCALES]};
+  uint4 q[kSMaxCh][kSRowsGU][2];
+  uint32_t sc[kSMaxCh][kSRowsGU][2];
+#pragma unroll
+  for (int u = 0; u < kSMaxCh; ++u) {
+    const int c = tid + 256 * u;
+#pragma unroll
+    for (int r = 0; r < kSRowsGU; ++r)
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        if (c < nch) {
+          const size_t row = (size_t)(i0 + r);
+          q[u][r][m] = *reinterpret_cast<const uint4*>(cb[m] + row * (H / 2) + 16 * c);
+          sc[u][r][m] = sscale<FMT>(sbp[m] + row * (H / B), c);
+        } else {
+          q[u][r][m] = make_uint4(0u, 0u, 0u, 0u);
+          sc[u][r][m] = 0u;
+        }
+      }
+  }
+  float acc[kSRowsGU][2];
+#pragma unroll
+  for (int r = 0; r < kSRowsGU; ++r) { acc[r][0] = 0.0f; acc[r][1] = 0.0f; }
+#pragma unroll
+  for (int u = 0; u < kSMaxCh; ++u) {
+    const int c = tid + 256 * u;
+    if (c < nch) {
+      float xv[32];
+      const float4* xp = reinterpret_cast<const float4*>(a.x + 32 * c);
+#pragma unroll
+      for (int v = 0; v < 8; ++v) {
+        const float4 f = xp[v];
+        xv[4 * v] = f.x; xv[4 * v + 1] = f.y; xv[4 * v + 2] = f.z; xv[4 * v + 3] = f.w;
+      }
+#pragma unroll
+      for (int r = 0; r < kSRowsGU; ++r)
+#pragma unroll
+        for (int m = 0; m < 2; ++m) acc[r][m] += sdot32<FMT>(q[u][r][m], sc[u][r][m], xv);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < kSRowsGU; ++r)
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const float v = wave_sum_dpp(acc[r][m]);
+      if (lane == 0) s_part[wave][2 * r + m] = v;
+    }
+  __syncthreads();
+  if (tid < kSRowsGU) {
+    float gv = ((s_part[0][2 * tid] + s_part[1][2 * tid]) + s_part[2][2 * tid]) + s_part[3][2 * tid];
+    float uv = ((s_part[0][2 * tid + 1] + s_part[1][2 * tid + 1]) + s_part[2][2 * tid + 1]) +
+               s_part[3][2 * tid + 1];
+    if (FMT == MOE_FMT_NVFP4) {
+      const float* gl = reinterpret_cast<const float*>(rec + a.off[MOE_T_GLOBALS]);
+      gv *= gl[0];
+      uv *= gl[1];
+    }
+    a.h[(size_t)j * a.I + i0 + tid] = gv / (1.0f + expf(-gv)) * uv;
+  }
+}
+
+// out rows n0 .. n0+7 = sum over shared experts of W_down h: the threads
+// split the concatenated K (every expert's I) into 32-element chunks.
+template <int FMT>
+__global__ __launch_bounds__(256) void k_sdn(SArgs a) {
+  constexpr int B = FMT == MOE_FMT_MXFP4 ? 32 : 16;
+  __shared__ float s_part[4][kSRowsDN];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int n0 = blockIdx.x * kSRowsDN, I = a.I, nchI = I / 32, ntot = a.ns * nchI;
+  uint4 q[kSMaxCh][kSRowsDN];
+  uint32_t sc[kSMaxCh][kSRowsDN];
+#pragma unroll
+  for (int u = 0; u < kSMaxCh; ++u) {
+    const int cc = tid + 256 * u;
+    const int j = cc < ntot ? cc / nchI : 0, c = cc < ntot ? cc - j * nchI : 0;
+    const uint8_t* rec = a.base + (size_t)j * a.stride;
+#pragma unroll
+    for (int r = 0; r < kSRowsDN; ++r) {
+      if (cc < ntot) {
+        const size_t row = (size_t)(n0 + r);
+        q[u][r] = *reinterpret_cast<const uint4*>(rec + a.off[MOE_T_DOWN_CODES] + row * (I / 2) + 16 * c);
+        sc[u][r] = sscale<FMT>(rec + a.off[MOE_T_DOWN_SCALES] + row * (I / B), c);
+      } else {
+        q[u][r] = make_uint4(0u, 0u, 0u, 0u);
+        sc[u][r] = 0u;
+      }
+    }
+  }
+  float acc[kSRowsDN];
+#pragma unroll
+  for (int r = 0; r < kSRowsDN; ++r) acc[r] = 0.0f;
+#pragma unroll
+  for (int u = 0; u < kSMaxCh; ++u) {
+    const int cc = tid + 256 * u;
+    if (cc < ntot) {
+      const int j = cc / nchI, c = cc - j * nchI;
+      float g = 1.0f;
+      if (FMT == MOE_FMT_NVFP4)
+        g = reinterpret_cast<const float*>(a.base + (size_t)j * a.stride + a.off[MOE_T_GLOBALS])[2];
+      float hv[32];
+      const float4* hp = reinterpret_cast<const float4*>(a.h + (size_t)j * I + 32 * c);
+#pragma unroll
+      for (int v = 0; v < 8; ++v) {
+        const float4 f = hp[v];
+        hv[4 * v] = f.x; hv[4 * v + 1] = f.y; hv[4 * v + 2] = f.z; hv[4 * v + 3] = f.w;
+      }
+#pragma unroll
+      for (int r = 0; r < kSRowsDN; ++r) acc[r] += g * sdot32<FMT>(q[u][r], sc[u][r], hv);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < kSRowsDN; ++r) {
+    const float v = wave_sum_dpp(acc[r]);
+    if (lane == 0) s_part[wave][r] = v;
+  }
+  __syncthreads();
+  if (tid < kSRowsDN)
+    a.out[n0 + tid] = ((s_part[0][tid] + s_part[1][tid]) + s_part[2][tid]) + s_part[3][tid];
+}
+
+bool shared1_ok(const moe_bank* S, int H) {
+  return S->hidden == H && H % 32 == 0 && S->inter % 32 == 0 && H / 32 <= 256 * kSMaxCh &&
+         S->num_experts * (S->inter / 32) <= 256 * kSMaxCh && H % kSRowsDN == 0 &&
+         S->inter % kSRowsGU == 0 && (S->format == MOE_FMT_MXFP4 || S->format == MOE_FMT_NVFP4);
+}
+
+moe_status launch_shared1(const moe_bank* S, const float* x, float* h, float* out, hipStream_t st) {
+  SArgs a;
+  a.base = static_cast<const uint8_t*>(S->base);
+  a.stride = S->expert_stride;
+  for (int t = 0; t < MOE_NUM_TENSORS; ++t) a.off[t] = S->offset[t];
+  a.ns = S->num_experts; a.H = S->hidden; a.I = S->inter;
+  a.x = x; a.h = h; a.out = out;
+  const dim3 ggu(a.I / kSRowsGU, a.ns), gdn(a.H / kSRowsDN);
+  if (S->format == MOE_FMT_MXFP4) {
+    hipLaunchKernelGGL(k_sgu<MOE_FMT_MXFP4>, ggu, dim3(256), 0, st, a);
+    hipLaunchKernelGGL(k_sdn<MOE_FMT_MXFP4>, gdn, dim3(256), 0, st, a);
+  } else {
+    hipLaunchKernelGGL(k_sgu<MOE_FMT_NVFP4>, ggu, dim3(256), 0, st, a);
+    hipLaunchKernelGGL(k_sdn<MOE_FMT_NVFP4>, gdn, dim3(256), 0, st, a);
+  }
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_DEVICE;
+}
+
 // Workspace of the latent layer: the routed experts', the router's and the
 // shared experts' workspaces, x_lat, y_lat, the routed selection and the
 // shared one.  The routed experts' region comes first, so that its error word
@@ -298,7 +508,9 @@ moe_status moe_latent_layer_fwd(const moe_latent_layer* layer, const float* x, i
   g.sel_idx = sidx; g.sel_w = sw; g.ns = ns;     // the shared experts' selection
   // and, where the decode-batch streams take the shared bank, its dispatch
   // table (every token, every shared expert), so no dispatch launch is needed
-  const bool shared_streams = bank_status(&S) == MOE_OK && batched_decode_shape(&S, C);
+  const bool shared_one = C == 1 && bank_status(&S) == MOE_OK && shared1_ok(&S, H);
+  const bool shared_streams =
+      !shared_one && bank_status(&S) == MOE_OK && batched_decode_shape(&S, C);
   const WsLayout Ls = ws_layout(ns, S.hidden, S.inter, ns, C);
   g.sel_disp = shared_streams ? reinterpret_cast<int32_t*>(w8 + W.shared + Ls.disp) : nullptr;
   moe_status s = launch_gemv(g, st);
@@ -313,7 +525,8 @@ moe_status moe_latent_layer_fwd(const moe_latent_layer* layer, const float* x, i
   }
   if (s != MOE_OK) return s;
   // finish phase: shared experts into out, then routed_norm and routed_up added
-  s = shared_streams
+  s = shared_one ? launch_shared1(&S, x, reinterpret_cast<float*>(w8 + W.shared + Ls.h), out, st)
+      : shared_streams
           ? launch_batched_decode(&S, x, C, ns, sidx, sw, out, w8 + W.shared, Ls, st)
           : moe_expert_fwd(&S, x, C, ns, sidx, sw, out, w8 + W.shared, ws_bytes_s, stream);
   if (s != MOE_OK) return s;

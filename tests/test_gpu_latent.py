@@ -61,8 +61,9 @@ def _small(fmt, C, k=8, ns=2):
                                 gamma_scale=2.0 ** 17)
 
 
-@pytest.mark.parametrize("C,fmt,k,ns", [(1, synth.FMT_NV, 8, 2), (5, synth.FMT_MX, 8, 2),
-                                        (16, synth.FMT_NV, 16, 3), (3, synth.FMT_MX, 1, 1)])
+@pytest.mark.parametrize("C,fmt,k,ns", [(1, synth.FMT_NV, 8, 2), (1, synth.FMT_MX, 4, 3),
+                                        (5, synth.FMT_MX, 8, 2), (16, synth.FMT_NV, 16, 3),
+                                        (3, synth.FMT_MX, 1, 1)])
 def test_latent_layer_parity(C, fmt, k, ns):
     wl = _small(fmt, C, k, ns)
     say(f"[latent] E={wl.E} k={k} H={wl.H} L={wl.L} shared={ns} C={C} fmt={fmt}")
