@@ -1518,10 +1518,10 @@ moe_status launch_route(const float* x, const float* Wr, const float* logits_in,
     a.ksplit = 1;
     a.kper = H;
   }
-  // Several tokens: the top-k (and the dispatch table) runs as its own
-  // launch, one wave per token, instead of token after token in the last
-  // workgroup.
-  a.select = (x && C > 1) ? 0 : 1;
+  // With x, the top-k (and the dispatch table) runs as its own launch, one
+  // wave per token, instead of in the router's last workgroup (one token:
+  // the one-wave selection of the separate launch is also the faster).
+  a.select = x ? 0 : 1;
   if (C == 1) hipLaunchKernelGGL(k_route<1>, dim3(grid), dim3(kWG), 0, st, a);
   else if (C <= 4) hipLaunchKernelGGL(k_route<4>, dim3(grid), dim3(kWG), 0, st, a);
   else hipLaunchKernelGGL(k_route<16>, dim3(grid), dim3(kWG), 0, st, a);
