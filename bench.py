@@ -113,6 +113,18 @@ def code_sha256(paths) -> str:
     return hashlib.sha256(text.encode()).hexdigest()
 
 
+def check_error_word(ws, what: str):
+    """The single-launch decode kernel sets the uint32 at byte 16 of its
+    workspace when one of its bounded waits gives up (its outputs are then
+    undefined): a timing taken with it set is not a measurement."""
+    import torch
+    torch.cuda.synchronize()
+    if int(ws.tensor[4].item()) != 0:
+        log(f"{what}: the decode kernel's error word is set (a bounded wait expired); "
+            "no figure is reported")
+        sys.exit(3)
+
+
 def expert_bytes(spec) -> int:
     return spec.expert_bytes()
 
@@ -247,6 +259,7 @@ def bench_latent(args, wl):
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    check_error_word(ws, "latent layer timing")
     ms_step = e0.elapsed_time(e1) / args.steps
     us_call = ms_step * 1000.0 / wl.layers
     uniq = np.mean([len(np.unique(idx[l][j].cpu().numpy())) for l in range(wl.layers)
@@ -385,6 +398,7 @@ def main():
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    check_error_word(ws, "layer timing")
     ms_step = e0.elapsed_time(e1) / args.steps
     us_call = ms_step * 1000.0 / wl.layers          # one moe_layer_fwd call (C tokens)
     us_layer = us_call / C                          # per token per MoE layer
@@ -426,6 +440,7 @@ def main():
 
     us_expert = timed(expert_step, args.steps) if not args.layer_only else float("nan")
     us_route = timed(route_step, args.steps) if not args.layer_only else float("nan")
+    check_error_word(ws, "expert-only timing")
     # distinct experts per call
     uniq = np.mean([len(np.unique(idx[l][j].cpu().numpy())) for l in range(wl.layers)
                     for j in range(pool)])

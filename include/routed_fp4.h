@@ -18,7 +18,9 @@
  *
  * Conventions for every entry point
  *  - All tensor pointers are DEVICE pointers owned by the caller; the library
- *    never allocates, frees or synchronises, and keeps no global state.
+ *    never allocates, frees or synchronises.  Its only global state is per
+ *    device and written once: the CU count, whether the single-launch decode
+ *    kernel fits (atomics, so concurrent first calls are safe).
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
  *    device work is enqueued on it; results are ready when the stream is.
  *  - Arguments are validated on the host before anything is enqueued; on error
@@ -215,16 +217,19 @@ moe_status moe_latent_layer_fwd(const moe_latent_layer *layer, const float *x, i
                                 void *ws, size_t ws_bytes, void *stream);
 
 /* MXFP4 experts on the block-scaled FP4 matrix cores (page "SparkInfer-K3",
- * section "Where to customize": without FP4 tensor cores every low-bit expert
- * product dequantises to bf16 first; CDNA4's v_mfma_scale_f32_16x16x128_f8f6f4
- * takes the MXFP4 codes and their e8m0 block scales as they are stored).
+ * Roadmap, "Later · B200 / B300 -- the Blackwell delta": without FP4 tensor
+ * cores every low-bit expert product dequantises to bf16 first; CDNA4's
+ * v_mfma_scale_f32_16x16x128_f8f6f4 takes the MXFP4 codes and their e8m0
+ * block scales as they are stored).
  * The same computation as moe_expert_fwd for an MXFP4 bank: the fp32
  * activations (x, and h after SwiGLU) enter as `terms` e4m3 terms with an
  * e8m0 scale per 32 values; terms = 1 is a lossy single-term mode, and each
- * further term takes about 4 more bits.  The instruction adds each group of
- * 8 products in fixed point about 13 bits below the group's largest
- * (measured), so the error levels off near 2e-5 rel-L2 from terms = 4 on:
- * a near-exact mode, not bit-for-bit the fp32 path.
+ * further term takes about 4 more bits.  The instruction truncates inside
+ * each group of 8 products below 2^(largest exponent sum - 13) (measured);
+ * the terms are built so that no product of a group falls below that
+ * quantum, so from terms = 4 on the result is within the library's bar
+ * (rel-L2 2e-5, max-abs 1e-4 of the largest output): a near-exact mode, not
+ * bit-for-bit the fp32 path.
  *  bank: MXFP4, hidden and inter multiples of 256.  1 <= C <= MOE_MAX_TOKENS,
  *  1 <= k <= min(E, MOE_MAX_TOPK), 1 <= terms <= 6.  x [C][H] and out [C][H]
  *  fp32, 16-byte aligned, not aliased; topk_idx / topk_w [C][k] (an

@@ -33,5 +33,29 @@ def hipcc(srcs, out: str, extra=()) -> str:
 
 
 def build_library() -> str:
-    """Compile the HIP kernels and the C ABI into libroutedfp4.so."""
-    return hipcc(SRCS, OUT)
+    """Compile the HIP kernels and the C ABI into libroutedfp4.so: one object
+    per source, compiled in parallel, then linked."""
+    from concurrent.futures import ThreadPoolExecutor
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    flags = [f for f in HIP_FLAGS if f != "-shared"]
+
+    def compile_one(src):
+        obj = os.path.join(objdir, os.path.basename(src) + ".o")
+        tmp = obj + ".tmp"
+        r = subprocess.run([HIPCC, *flags, f"-I{INCLUDE}", "-c", src, "-o", tmp],
+                           capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
+        os.replace(tmp, obj)
+        return obj
+
+    with ThreadPoolExecutor(max_workers=min(len(SRCS), 8)) as ex:
+        objs = list(ex.map(compile_one, SRCS))
+    tmp = OUT + ".tmp"
+    r = subprocess.run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stderr}")
+    os.replace(tmp, OUT)
+    return OUT

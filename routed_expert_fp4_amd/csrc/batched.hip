@@ -533,13 +533,22 @@ __global__ __launch_bounds__(256) void k_brouter(const float* x, const float* Wr
       wsm[r][c4] = wv.x; wsm[r][c4 + 1] = wv.y; wsm[r][c4 + 2] = wv.z; wsm[r][c4 + 3] = wv.w;
     }
     __syncthreads();
+    // The instruction adds its 4 products to the accumulator as 4 chained
+    // FMAs (measured), so a chunk's products go into an accumulator of their
+    // own (32 roundings) that is then added to the running sum: the longest
+    // rounding chain of a logit is 32 + H/32 instead of H.
+    f32x4_t part[4];
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) part[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < kRK; kk += 4) {
       const float av = xsm[16 * wave + r16][kk + g];
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb)
-        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, wsm[nb * 16 + r16][kk + g], acc[nb], 0, 0, 0);
+        part[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, wsm[nb * 16 + r16][kk + g], part[nb], 0, 0, 0);
     }
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) acc[nb] += part[nb];
   }
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) {

@@ -33,6 +33,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "routed_fp4.h"
 #include "common.h"
 
@@ -1435,16 +1437,16 @@ __global__ void k_fill_zero(uint32_t* p, size_t n) {
 // Host side
 // ---------------------------------------------------------------------------
 int device_cu_count() {
-  static int cache[64] = {0};
+  static std::atomic<int> cache[64];   // per device, 0 until first asked
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cache[dev] == 0) {
-    int n = 0;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
       n = 256;
-    cache[dev] = n;
+    cache[dev].store(n, std::memory_order_relaxed);
   }
-  return cache[dev];
+  return n;
 }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
@@ -1583,17 +1585,21 @@ struct Moe1Shape {
 
 template <int FMT, int KG, int KD, int SGU, int SDN, int KT, bool XR = false>
 moe_status launch_moe1_kernel(Moe1Args a, hipStream_t st) {
-  static int ok_dev[64] = {0};   // 1: kG1 workgroups fit at once on this device, -1: they do not
+  // per device: 1 = kG1 workgroups fit at once, -1 = they do not (0: not yet known)
+  static std::atomic<int> ok_dev[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  if (ok_dev[dev] == 0) {
+  int ok = ok_dev[dev].load(std::memory_order_relaxed);
+  if (ok == 0) {
+    // two threads may both query; they store the same answer
     int per_cu = 0;
     const bool fits = hipOccupancyMaxActiveBlocksPerMultiprocessor(
                           &per_cu, k_moe1<FMT, KG, KD, SGU, SDN, KT, XR>, kWG1, 0) == hipSuccess &&
                       per_cu * device_cu_count() >= kG1;
-    ok_dev[dev] = fits ? 1 : -1;
+    ok = fits ? 1 : -1;
+    ok_dev[dev].store(ok, std::memory_order_relaxed);
   }
-  if (ok_dev[dev] < 0) return MOE_ERR_UNSUPPORTED;
+  if (ok < 0) return MOE_ERR_UNSUPPORTED;
   // A plain launch: with at most one workgroup per CU and kG1 <= the CUs
   // that can hold one, every workgroup is resident once the stream's earlier
   // work has drained, so every wait ends.  (The cooperative launch API gives

@@ -18,3 +18,24 @@ def orc():
     import oracle
     oracle.build()
     return oracle
+
+
+def pytest_terminal_summary(terminalreporter):
+    """Near-tie tokens of every GPU selection check (tokens whose GPU and
+    oracle selections differ only by reordering logits within the certified
+    rounding bound), so the count stays in the log of a quiet run."""
+    try:
+        import gpu_util
+    except ImportError:
+        return
+    if not gpu_util.NEAR_TIES:
+        return
+    rows = gpu_util.NEAR_TIES
+    terminalreporter.section("near-tie tokens per selection check")
+    tot_t = sum(r[1] for r in rows)
+    tot_n = sum(r[2] for r in rows)
+    for test, n, near in rows:
+        if near:
+            terminalreporter.write_line(f"{test}: {near} of {n}")
+    terminalreporter.write_line(f"all checks: {tot_n} near-tie tokens of {tot_t} "
+                                f"({len(rows)} checks, {sum(1 for r in rows if r[2])} with any)")
