@@ -20,7 +20,8 @@
  *  - All tensor pointers are DEVICE pointers owned by the caller; the library
  *    never allocates, frees or synchronises.  Its only global state is per
  *    device and written once: the CU count, whether the single-launch decode
- *    kernel fits (atomics, so concurrent first calls are safe).
+ *    kernel fits (atomics, so concurrent first calls are safe), and the
+ *    device array of moe_layer_fwd_noalloc.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
  *    device work is enqueued on it; results are ready when the stream is.
  *  - Arguments are validated on the host before anything is enqueued; on error
@@ -240,6 +241,27 @@ size_t moe_mx_mma_workspace_size(const moe_bank *bank, int32_t top_k, int32_t C,
 moe_status moe_expert_fwd_mx_mma(const moe_bank *bank, const float *x, int32_t C, int32_t k,
                                  const int32_t *topk_idx, const float *topk_w, float *out,
                                  int32_t terms, void *ws, size_t ws_bytes, void *stream);
+
+/* moe_layer_fwd for callers that cannot allocate device memory (code under
+ * HIP graph capture, serving loops that must not call the allocator): the
+ * same arguments without a workspace, which is instead a device array of the
+ * library's own, one per GPU, 40 MiB, held until the process ends.  Its
+ * limit covers every call of up to MOE_MAX_DECODE_TOKENS tokens at every
+ * supported shape (the largest, E 1024, H 8192, I 4096, k 32, C 16, needs
+ * 37.4 MiB) and the K3 shape up to 64 tokens; calls whose moe_workspace_size
+ * exceeds it return MOE_ERR_WORKSPACE with nothing enqueued.
+ *  - The first call on a device zero-fills the array (a fill kernel on
+ *    `stream`); every call on that GPU shares it and leaves it ready for the
+ *    next, so calls that overlap on one GPU (other streams, other threads)
+ *    race and must be serialised by the caller.
+ *  - error_out: NULL, or a device int32 that receives the decode kernel's
+ *    error word (1 if one of its bounded waits expired during this or an
+ *    earlier call, whose outputs are then undefined; see above), which is
+ *    then cleared; one extra one-thread launch.
+ * Otherwise as moe_layer_fwd (arguments, errors, outputs). */
+moe_status moe_layer_fwd_noalloc(const moe_bank *bank, const float *w_router, const float *x,
+                                 int32_t C, int32_t k, float *out, int32_t *topk_idx_out,
+                                 float *topk_w_out, int32_t *error_out, void *stream);
 
 /* Test export: dequantise one matrix of one expert to fp32.
  *  matrix 0 = gate [I][H], 1 = up [I][H], 2 = down [H][I].

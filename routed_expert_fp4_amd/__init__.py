@@ -27,7 +27,7 @@ BLOCK = {MOE_FMT_MXFP4: 32, MOE_FMT_NVFP4: 16}
 EXPORTS = ("moe_version", "moe_status_string", "moe_bank_layout", "moe_workspace_size",
            "moe_workspace_init", "moe_route", "moe_expert_fwd", "moe_layer_fwd", "moe_dequant",
            "moe_latent_workspace_size", "moe_latent_layer_fwd", "moe_mx_mma_workspace_size",
-           "moe_expert_fwd_mx_mma")
+           "moe_expert_fwd_mx_mma", "moe_layer_fwd_noalloc")
 
 
 class MoeError(RuntimeError):
@@ -76,6 +76,7 @@ def lib() -> ctypes.CDLL:
             "moe_latent_layer_fwd": ([P, P, i32, i32, P, P, P, P, sz, P], i32),
             "moe_mx_mma_workspace_size": ([P, i32, i32, i32], sz),
             "moe_expert_fwd_mx_mma": ([P, P, i32, i32, P, P, P, i32, P, sz, P], i32),
+            "moe_layer_fwd_noalloc": ([P, P, P, i32, i32, P, P, P, P, P], i32),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -215,6 +216,19 @@ def moe_layer_fwd(bank: Bank, w_router, x, C, k, out, topk_idx_out=None, topk_w_
         _ptr(x, torch.float32, (C, H), "x"), C, k, _ptr(out, torch.float32, (C, H), "out"),
         _ptr(topk_idx_out, torch.int32, (C, k), "topk_idx_out"),
         _ptr(topk_w_out, torch.float32, (C, k), "topk_w_out"), ws.ptr, ws.nbytes, _stream(stream)))
+
+
+def moe_layer_fwd_noalloc(bank: Bank, w_router, x, C, k, out, topk_idx_out=None,
+                          topk_w_out=None, error_out=None, stream=None):
+    """moe_layer_fwd on the library's own device array instead of a workspace."""
+    import torch
+    H, E = bank.H, bank.E
+    _check("moe_layer_fwd_noalloc", lib().moe_layer_fwd_noalloc(
+        _bank(bank), _ptr(w_router, torch.float32, (E, H), "w_router"),
+        _ptr(x, torch.float32, (C, H), "x"), C, k, _ptr(out, torch.float32, (C, H), "out"),
+        _ptr(topk_idx_out, torch.int32, (C, k), "topk_idx_out"),
+        _ptr(topk_w_out, torch.float32, (C, k), "topk_w_out"),
+        _ptr(error_out, torch.int32, (1,), "error_out"), _stream(stream)))
 
 
 def moe_dequant(bank: Bank, expert: int, matrix: int, out, stream=None):

@@ -11,7 +11,8 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SRCS = [os.path.join(HERE, "csrc", "routed_fp4.hip"), os.path.join(HERE, "csrc", "batched.hip"),
-        os.path.join(HERE, "csrc", "latent.hip"), os.path.join(HERE, "csrc", "mxmma.hip")]
+        os.path.join(HERE, "csrc", "latent.hip"), os.path.join(HERE, "csrc", "mxmma.hip"),
+        os.path.join(HERE, "csrc", "noalloc.hip")]
 OUT = os.path.join(HERE, "libroutedfp4.so")
 INCLUDE = os.path.join(ROOT, "include")
 
