@@ -808,9 +808,6 @@ struct Moe1Shared {
     float hs[kMaxI1 + kMaxI1 / 8];   // h of the slot (down)
   } u;
   SelectLds sel;                   // wave 0's selection scratch
-  uint32_t lkey[MOE_MAX_EXPERTS];  // the selection's 32-bit logit keys
-  float lval[MOE_MAX_EXPERTS];     // ... and logits
-  int ncand;
   float ys[kWG1];                  // the combine's slot results [k][H / kG1]
   int32_t sidx[MOE_MAX_TOPK];
   float sw[MOE_MAX_TOPK];
@@ -885,110 +882,98 @@ __device__ __forceinline__ void moe1_router_finish(const Moe1Args& a, Moe1Shared
 }
 
 // The selection, computed by every workgroup for itself from the tagged
-// logits (or taken from the caller when the selection is given): all eight
-// waves poll and gather the candidates above a threshold, wave 0 ranks them
-// (the same exact top-k as wave_select, which remains the fallback).
+// logits (or taken from the caller when the selection is given), by wave 0
+// alone while the other waves wait at the closing barrier: it polls all E
+// logits of one replica (lane l holds experts l + 64 i), reading again only
+// the entries that do not yet carry this call's epoch; then a threshold on
+// the lane maxima, the candidates above it gathered to LDS, each ranked by
+// the number of candidates ahead of it (the same exact top-k as
+// wave_select, which remains the fallback for clustered winners).
 __device__ __forceinline__ void moe1_routing(const Moe1Args& a, Moe1Shared& S, uint32_t epoch, bool writer) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int k = a.k;
   constexpr int NPL = MOE_MAX_EXPERTS / 64;
   if (a.Wr) {
-    // Wave w polls experts e = 128 w + lane + 64 j (j < 2) of one replica.
-    const __amdgpu_buffer_rsrc_t lr = coherent_view(
-        a.tlogits + (size_t)(blockIdx.x % kLogitCopies) * 2 * a.E, (uint32_t)a.E * 16);
-    float lv[2];
-    uint32_t kv[2];
-    for (uint32_t it = 0;; ++it) {
-      uint4 t[2];                                // {half 0, tag, half 1, tag}
-#pragma unroll
-      for (int j = 0; j < 2; ++j) t[j] = coherent_ld_u4(lr, (uint32_t)(128 * wave + lane + 64 * j) * 16);
-      bool missing = false;
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int e = 128 * wave + lane + 64 * j;
-        const bool in = e < a.E;
-        missing |= in && (t[j].y != epoch || t[j].w != epoch);
-        lv[j] = in ? __uint_as_float(t[j].x) + __uint_as_float(t[j].z) : 0.0f;
-        kv[j] = in ? logit_key(lv[j]) : 0u;
-      }
-      if (!wg_any(missing, &S.flag)) break;
-      if (it == kSpinLimit) {
-        if (threadIdx.x == 0)
-          __hip_atomic_store(&a.ctrl[kCtrlErr], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        break;
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      S.lkey[128 * wave + lane + 64 * j] = kv[j];
-      S.lval[128 * wave + lane + 64 * j] = lv[j];
-    }
-    if (threadIdx.x == 0) S.ncand = 0;
-    __syncthreads();
-    // Every wave computes the same threshold T: with lane l holding experts
-    // l + 64 i, T is the largest t such that k lane maxima are >= t (a
-    // bit-by-bit search on the orderable 32-bit keys).  Those k lanes hold k
-    // experts with keys >= T, so every expert of the top k has a key >= T.
-    uint32_t m = 0;
-#pragma unroll
-    for (int i = 0; i < NPL; ++i) {
-      const int e = lane + 64 * i;
-      const uint32_t kk = e < a.E ? S.lkey[e] : 0u;
-      m = kk > m ? kk : m;
-    }
-    uint32_t T = 0;
-    for (int bit = 31; bit >= 0; --bit) {
-      const uint32_t c = T | (1u << bit);
-      if (__popcll(__ballot(m >= c)) >= k) T = c;
-    }
-    // The candidates (keys >= T; usually a few more than k) gather in LDS,
-    // each wave adding the ones it polled.
-    bool cand[2];
-    int nmine = 0;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      cand[j] = 128 * wave + lane + 64 * j < a.E && kv[j] >= T;
-      nmine += __popcll(__ballot(cand[j]));
-    }
-    int base = 0;
-    if (lane == 0 && nmine) base = atomicAdd(&S.ncand, nmine);
-    base = __builtin_amdgcn_readfirstlane(base);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const unsigned long long bal = __ballot(cand[j]);
-      const int pos = base + __popcll(bal & ((1ull << lane) - 1ull));
-      if (cand[j] && pos < 64) {
-        const int e = 128 * wave + lane + 64 * j;
-        S.sel.cand_key[pos] = ((uint64_t)kv[j] << 32) | (uint64_t)(~(uint32_t)e);
-        S.sel.cand_l[pos] = lv[j];
-      }
-      base += __popcll(bal);
-    }
-    __syncthreads();
     if (wave == 0) {
-      const int n = S.ncand;
+      const __amdgpu_buffer_rsrc_t lr = coherent_view(
+          a.tlogits + (size_t)(blockIdx.x % kLogitCopies) * 2 * a.E, (uint32_t)a.E * 16);
+      uint4 t[NPL];                                  // {half 0, tag, half 1, tag}
+      bool need[NPL];
+#pragma unroll
+      for (int i = 0; i < NPL; ++i) {
+        need[i] = lane + 64 * i < a.E;
+        t[i] = make_uint4(0u, 0u, 0u, 0u);
+      }
+      for (uint32_t it = 0;; ++it) {
+#pragma unroll
+        for (int i = 0; i < NPL; ++i)
+          if (need[i]) t[i] = coherent_ld_u4(lr, (uint32_t)(lane + 64 * i) * 16);
+        bool missing = false;
+#pragma unroll
+        for (int i = 0; i < NPL; ++i) {
+          need[i] = need[i] && (t[i].y != epoch || t[i].w != epoch);
+          missing |= need[i];
+        }
+        if (!__any(missing)) break;
+        if (it == kSpinLimit) {
+          if (lane == 0)
+            __hip_atomic_store(&a.ctrl[kCtrlErr], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+      }
+      uint64_t ck[NPL];
+      float lv[NPL];
+      uint32_t m = 0;                                // this lane's largest 32-bit key
+#pragma unroll
+      for (int i = 0; i < NPL; ++i) {
+        const int e = lane + 64 * i;
+        const bool in = e < a.E;
+        lv[i] = in ? __uint_as_float(t[i].x) + __uint_as_float(t[i].z) : 0.0f;
+        const uint32_t kk = in ? logit_key(lv[i]) : 0u;
+        ck[i] = in ? (((uint64_t)kk << 32) | (uint64_t)(~(uint32_t)e)) : 0;
+        m = kk > m ? kk : m;
+      }
+      // T: the largest t whose low 16 bits are zero such that k lane maxima
+      // are >= t (a bit-by-bit search over the upper half of the orderable
+      // keys).  Those k lanes hold k experts with keys >= T, so every expert
+      // of the top k has a key >= T; the candidates are the (usually few
+      // more than k) experts at or above it.
+      uint32_t T = 0;
+      for (int bit = 31; bit >= 16; --bit) {
+        const uint32_t c = T | (1u << bit);
+        if (__popcll(__ballot(m >= c)) >= k) T = c;
+      }
+      int n = 0;
+#pragma unroll
+      for (int i = 0; i < NPL; ++i) {
+        const bool c = ck[i] != 0 && (uint32_t)(ck[i] >> 32) >= T;
+        const unsigned long long bal = __ballot(c);
+        const int pos = n + __popcll(bal & ((1ull << lane) - 1ull));
+        if (c && pos < 64) {
+          S.sel.cand_key[pos] = ck[i];
+          S.sel.cand_l[pos] = lv[i];
+        }
+        n += __popcll(bal);
+      }
       if (n <= 64) {
-        // rank = number of candidates ahead (larger key; equal logits: lower index)
+        // zero keys after the last candidate up to a multiple of 4 (never ahead of a real key)
+        if (lane >= n && lane < ((n + 3) & ~3)) S.sel.cand_key[lane] = 0;
+        wave_lds_fence();
         const uint64_t mine = lane < n ? S.sel.cand_key[lane] : 0;
         const float ml = lane < n ? S.sel.cand_l[lane] : 0.0f;
-        int rk = 0;
-        for (int j = 0; j < n; ++j) rk += readlane_u64(mine, j) > mine ? 1 : 0;
+        int rk = 0;                                  // candidates ahead (broadcast LDS reads)
+        for (int j = 0; j < n; j += 4) {
+          const uint64_t c0 = S.sel.cand_key[j], c1 = S.sel.cand_key[j + 1];
+          const uint64_t c2 = S.sel.cand_key[j + 2], c3 = S.sel.cand_key[j + 3];
+          rk += (c0 > mine) + (c1 > mine) + (c2 > mine) + (c3 > mine);
+        }
         if (lane < n && rk < k) {
           S.sel.sel_e[rk] = (int32_t)~(uint32_t)mine;
           S.sel.sel_l[rk] = ml;
         }
         wave_lds_fence();
       } else {
-        // clustered winners: the general one-wave selection over all experts
-        uint64_t ck[NPL];
-        float lw[NPL];
-#pragma unroll
-        for (int i = 0; i < NPL; ++i) {
-          const int e = lane + 64 * i;
-          lw[i] = e < a.E ? S.lval[e] : 0.0f;
-          ck[i] = e < a.E ? (((uint64_t)S.lkey[e] << 32) | (uint64_t)(~(uint32_t)e)) : 0;
-        }
-        wave_select<NPL>(ck, lw, k, S.sel);
+        wave_select<NPL>(ck, lv, k, S.sel);          // clustered winners
       }
       const float l = lane < k ? S.sel.sel_l[lane] : 0.0f;
       const float w = route_weight(l, lane, k);
