@@ -52,6 +52,8 @@ def parse():
                    help="tokens per call instead of the workload's own (a sweep over C reuses "
                         "one workload's bank, routing and shapes)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-read-calibration", action="store_true",
+                   help="skip measuring the achievable read rate beside the result")
     p.add_argument("--cpu-layers", type=int, default=1,
                    help="layer-tokens of the workload the CPU oracle is timed on")
     p.add_argument("--layer-only", action="store_true",
@@ -63,6 +65,9 @@ def parse():
                         "call) instead of moe_layer_fwd")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run a plain 2 GiB device copy (HBM counter calibration)")
+    p.add_argument("--calibrate-read", action="store_true",
+                   help="only measure the achievable HBM read rate (a plain streaming read "
+                        "over 16 GiB, and single launches of one K3 layer's bytes) and print it")
     return p.parse_args()
 
 
@@ -75,6 +80,51 @@ def calibrate_copy():
         dst.copy_(src)
     torch.cuda.synchronize()
     log(f"copied {n} bytes x 3")
+
+
+def read_bandwidth(window_bytes: int = 323_018_944, total_gib: int = 16, passes: int = 4):
+    """The achievable HBM read rate on this GPU, measured with a plain
+    streaming read (synth.device.stream_read: 16-byte non-temporal loads,
+    2048 workgroups of 256 threads, grid-stride):
+
+    * streaming: the whole 16 GiB buffer (64x the 256 MB last-level cache)
+      per launch, best of `passes`;
+    * single launch: one launch per window of `window_bytes` (by default one
+      K3 layer call's algorithmic bytes), consecutive launches reading
+      consecutive windows of the 16 GiB buffer so that no window is read
+      twice within 50 launches; the average per launch, ramp and tail
+      included (the same situation as one layer kernel).
+    Returns (streaming GB/s, single-launch GB/s)."""
+    import torch
+    import synth.device as sd
+    n = total_gib << 30
+    buf = torch.empty(n, dtype=torch.uint8, device="cuda")
+    blocks = 2048
+    sink = torch.empty(blocks, dtype=torch.int32, device="cuda")
+    st = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    sd.stream_read(buf.data_ptr(), n, blocks, sink.data_ptr(), st.cuda_stream)     # warm-up
+    best = 0.0
+    for _ in range(passes):
+        a.record(st)
+        sd.stream_read(buf.data_ptr(), n, blocks, sink.data_ptr(), st.cuda_stream)
+        b.record(st)
+        torch.cuda.synchronize()
+        best = max(best, n / (a.elapsed_time(b) * 1e-3) / 1e9)
+    w = (window_bytes + 4095) // 4096 * 4096
+    nwin = n // w
+    launches = 200
+    a.record(st)
+    for i in range(launches):
+        off = (i % nwin) * w
+        sd.stream_read(buf.data_ptr() + off, window_bytes // 16 * 16, blocks, sink.data_ptr(),
+                       st.cuda_stream)
+    b.record(st)
+    torch.cuda.synchronize()
+    single = window_bytes // 16 * 16 * launches / (a.elapsed_time(b) * 1e-3) / 1e9
+    del buf
+    torch.cuda.empty_cache()
+    return best, single
 
 
 KERNEL_SRC = tuple(os.path.join(ROOT, "routed_expert_fp4_amd", "csrc", f)
@@ -129,47 +179,74 @@ def expert_bytes(spec) -> int:
     return spec.expert_bytes()
 
 
-def cpu_baseline(wl, layers: int, max_tokens: int = 8):
+def cpu_baseline(wl, layers: int, max_tokens: int = 8, threads: int = 0, max_experts: int = 0):
     """The oracle as it is, on `layers` layer calls of the workload with at
     most `max_tokens` tokens each (the first tokens of the call); input
     regeneration (the synthetic bank bytes) is excluded from the timing.  Each
-    distinct selected expert is dequantised once per call."""
+    distinct selected expert is dequantised once per call.  threads: the
+    oracle's OpenMP threads (0: all it has).  max_experts > 0 times only the
+    first max_experts distinct experts of each call and scales their time by
+    the call's (token, slot) pairs over the sampled experts' pairs (the
+    router, top-k, weights and combine are timed whole)."""
     import numpy as np
     import oracle
     import synth
     oracle.build()
-    total = 0.0
-    C = min(wl.C, max_tokens)
-    for l in range(layers):
-        spec = wl.bank(l % wl.layers)
-        Wr, x = synth.layer_inputs(wl, l % wl.layers, pool=0)
-        x = np.ascontiguousarray(x[:C])
-        L = oracle.router_logits(x, Wr)
-        idx = oracle.topk(L, wl.k)
-        tensors = {int(e): synth.expert_tensors(spec, int(e)) for e in np.unique(idx)}
-        t0 = time.perf_counter()
-        L = oracle.router_logits(x, Wr)
-        idx = oracle.topk(L, wl.k)
-        ys = np.empty((C, wl.k, wl.H))
-        for e in np.unique(idx):
-            t = tensors[int(e)]
-            g = t["globals"]
-            Wg = oracle.dequant(spec.fmt, t["gate_codes"], t["gate_scales"], g[0])
-            Wu = oracle.dequant(spec.fmt, t["up_codes"], t["up_scales"], g[1])
-            Wd = oracle.dequant(spec.fmt, t["down_codes"], t["down_scales"], g[2])
-            for tok, slot in zip(*np.nonzero(idx == e)):
-                ys[tok, slot] = oracle.expert_ffn(Wg, Wu, Wd, x[tok])
-        for tok in range(C):
-            w = oracle.route_weights(L[tok, idx[tok]])
-            oracle.combine(w, ys[tok])
-        total += time.perf_counter() - t0
+    L_ = oracle.lib()
+    prev = int(L_.orc_threads())
+    if threads:
+        L_.orc_set_threads(threads)
+    try:
+        total = 0.0
+        C = min(wl.C, max_tokens)
+        sampled = []
+        for l in range(layers):
+            spec = wl.bank(l % wl.layers)
+            Wr, x = synth.layer_inputs(wl, l % wl.layers, pool=0)
+            x = np.ascontiguousarray(x[:C])
+            L = oracle.router_logits(x, Wr)
+            idx = oracle.topk(L, wl.k)
+            uniq = np.unique(idx)
+            take = uniq if not max_experts else uniq[:max_experts]
+            tensors = {int(e): synth.expert_tensors(spec, int(e)) for e in take}
+            t0 = time.perf_counter()
+            L = oracle.router_logits(x, Wr)
+            idx = oracle.topk(L, wl.k)
+            t_route = time.perf_counter() - t0
+            ys = np.zeros((C, wl.k, wl.H))
+            t1 = time.perf_counter()
+            pairs = 0
+            for e in take:
+                t = tensors[int(e)]
+                g = t["globals"]
+                Wg = oracle.dequant(spec.fmt, t["gate_codes"], t["gate_scales"], g[0])
+                Wu = oracle.dequant(spec.fmt, t["up_codes"], t["up_scales"], g[1])
+                Wd = oracle.dequant(spec.fmt, t["down_codes"], t["down_scales"], g[2])
+                for tok, slot in zip(*np.nonzero(idx == e)):
+                    ys[tok, slot] = oracle.expert_ffn(Wg, Wu, Wd, x[tok])
+                    pairs += 1
+            t_exp = (time.perf_counter() - t1) * (C * wl.k / pairs)
+            t2 = time.perf_counter()
+            for tok in range(C):
+                w = oracle.route_weights(L[tok, idx[tok]])
+                oracle.combine(w, ys[tok])
+            total += t_route + t_exp + (time.perf_counter() - t2)
+            sampled.append(len(take))
+        cores = int(L_.orc_threads())
+    finally:
+        L_.orc_set_threads(prev)
     us = total / (layers * C) * 1e6
     sample = f"{layers} layer call(s) of {C} token(s) of the same workload (pool draw 0"
     if C < wl.C:
         sample += f", the first {C} of the call's {wl.C} tokens"
-    sample += ("): router, top-k, weights, dequantisation of each distinct selected expert, "
-               "the expert FFNs and the combine; bank byte regeneration not timed")
-    return {"value": us, "unit": "us/token per MoE layer", "cores": int(oracle.lib().orc_threads()),
+    sample += "): router, top-k, weights, "
+    if max_experts:
+        sample += (f"dequantisation and FFNs of {sampled[0]} of the call's distinct selected "
+                   f"experts, their time scaled by all (token, slot) pairs over theirs, ")
+    else:
+        sample += "dequantisation of each distinct selected expert, the expert FFNs, "
+    sample += "and the combine; bank byte regeneration not timed"
+    return {"value": us, "unit": "us/token per MoE layer", "cores": cores,
             "kind": "oracle", "sample": sample}
 
 
@@ -320,6 +397,18 @@ def main():
 
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.calibrate_read:
+        import synth.device as sd
+        if not os.path.exists(sd.LIB):
+            sd.build()
+        torch.cuda.set_device(0)
+        streaming, single = read_bandwidth()
+        print(json.dumps({"calibration": "HBM read rate, plain streaming read (16-byte "
+                                         "non-temporal loads)",
+                          "streaming_16GiB_gbps": round(streaming, 1),
+                          "single_launch_323MB_gbps": round(single, 1),
+                          "peak_gbps": HBM_PEAK_GBPS}), flush=True)
         return
 
     import routed_expert_fp4_amd as rf
@@ -504,9 +593,20 @@ def main():
                      "us_per_launch": round(us_call, 3)},
         "wall_s_timed": round(wall, 3),
     }
+    if not args.no_read_calibration:
+        streaming, single = read_bandwidth(window_bytes=max(16, int(alg_bytes) // 16 * 16))
+        result["roofline"]["achievable_read_gbps"] = {
+            "streaming_16GiB": round(streaming, 1),
+            "single_launch_same_bytes": round(single, 1),
+            "how": "plain streaming read (bench.py --calibrate-read), one launch per window of "
+                   "the layer kernel's algorithmic bytes"}
+        result["roofline"]["frac_of_single_launch_read"] = round(gbps_kernel / single, 4)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle ...")
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_layers)
+        log("timing the CPU oracle on one core (sampled experts) ...")
+        result["cpu_baseline_1core"] = cpu_baseline(wl, 1, threads=1,
+                                                    max_experts=2 if wl.C == 1 else 4)
     print(json.dumps(result), flush=True)
 
 

@@ -943,17 +943,24 @@ __device__ __forceinline__ void moe1_routing(const Moe1Args& a, Moe1Shared& S, u
         const uint32_t c = T | (1u << bit);
         if (__popcll(__ballot(m >= c)) >= k) T = c;
       }
-      int n = 0;
+      // candidates: a bit per entry, placed by a prefix count over the lanes
+      uint32_t cm = 0;
+#pragma unroll
+      for (int i = 0; i < NPL; ++i)
+        cm |= (ck[i] != 0 && (uint32_t)(ck[i] >> 32) >= T) ? (1u << i) : 0u;
+      const int cnt = __popc(cm);
+      const int incl = wave_incl_scan(cnt);
+      const int n = __builtin_amdgcn_readlane(incl, 63);
+      int pos = incl - cnt;
 #pragma unroll
       for (int i = 0; i < NPL; ++i) {
-        const bool c = ck[i] != 0 && (uint32_t)(ck[i] >> 32) >= T;
-        const unsigned long long bal = __ballot(c);
-        const int pos = n + __popcll(bal & ((1ull << lane) - 1ull));
-        if (c && pos < 64) {
-          S.sel.cand_key[pos] = ck[i];
-          S.sel.cand_l[pos] = lv[i];
+        if ((cm >> i) & 1u) {
+          if (pos < 64) {
+            S.sel.cand_key[pos] = ck[i];
+            S.sel.cand_l[pos] = lv[i];
+          }
+          ++pos;
         }
-        n += __popcll(bal);
       }
       if (n <= 64) {
         // zero keys after the last candidate up to a multiple of 4 (never ahead of a real key)
@@ -961,6 +968,7 @@ __device__ __forceinline__ void moe1_routing(const Moe1Args& a, Moe1Shared& S, u
         wave_lds_fence();
         const uint64_t mine = lane < n ? S.sel.cand_key[lane] : 0;
         const float ml = lane < n ? S.sel.cand_l[lane] : 0.0f;
+        const float sg = 1.0f / (1.0f + expf(-ml));  // independent of the rank
         int rk = 0;                                  // candidates ahead (broadcast LDS reads)
         for (int j = 0; j < n; j += 4) {
           const uint64_t c0 = S.sel.cand_key[j], c1 = S.sel.cand_key[j + 1];
@@ -969,20 +977,30 @@ __device__ __forceinline__ void moe1_routing(const Moe1Args& a, Moe1Shared& S, u
         }
         if (lane < n && rk < k) {
           S.sel.sel_e[rk] = (int32_t)~(uint32_t)mine;
-          S.sel.sel_l[rk] = ml;
+          S.sel.sel_l[rk] = sg;                      // here the sigmoid, not the logit
         }
         wave_lds_fence();
+        // the weights in slot order: sigmoid / the sum over the k slots
+        const float sgk = lane < k ? S.sel.sel_l[lane] : 0.0f;
+        const float w = sgk / wave_sum(sgk);
+        if (lane < k) {
+          const int e = S.sel.sel_e[lane];
+          S.sidx[lane] = e;
+          S.sw[lane] = w;
+          if (writer && a.idx_out) a.idx_out[lane] = e;
+          if (writer && a.w_out) a.w_out[lane] = w;
+        }
       } else {
         wave_select<NPL>(ck, lv, k, S.sel);          // clustered winners
-      }
-      const float l = lane < k ? S.sel.sel_l[lane] : 0.0f;
-      const float w = route_weight(l, lane, k);
-      if (lane < k) {
-        const int e = S.sel.sel_e[lane];
-        S.sidx[lane] = e;
-        S.sw[lane] = w;
-        if (writer && a.idx_out) a.idx_out[lane] = e;
-        if (writer && a.w_out) a.w_out[lane] = w;
+        const float l = lane < k ? S.sel.sel_l[lane] : 0.0f;
+        const float w = route_weight(l, lane, k);
+        if (lane < k) {
+          const int e = S.sel.sel_e[lane];
+          S.sidx[lane] = e;
+          S.sw[lane] = w;
+          if (writer && a.idx_out) a.idx_out[lane] = e;
+          if (writer && a.w_out) a.w_out[lane] = w;
+        }
       }
     }
   } else if (threadIdx.x < k) {

@@ -1,9 +1,12 @@
-"""Device-side fill of synthetic expert banks (input generation only).
+"""Device-side fill of synthetic expert banks (input generation only), and the
+bench's read-bandwidth calibration.
 
 ``fill_bank`` writes every tensor of every expert of a bank with the same
 counter-based bytes that ``synth.expert_tensor_bytes`` regenerates on the host.
 Where the tensors sit inside an expert record (offsets, stride) is given by the
 caller, so this module knows nothing of any kernel's layout choices.
+``stream_read`` is a plain streaming read, the yardstick for the achievable
+HBM read rate that bench.py reports beside the 8 TB/s peak.
 """
 from __future__ import annotations
 
@@ -43,6 +46,9 @@ def lib():
                                         ctypes.c_int32, ctypes.c_uint64, ctypes.c_int32,
                                         ctypes.c_void_p]
         L.synth_fill_tensor.restype = ctypes.c_int
+        L.synth_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                                        ctypes.c_void_p, ctypes.c_void_p]
+        L.synth_stream_read.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -59,3 +65,12 @@ def fill_bank(ptr: int, offsets, stride: int, spec: BankSpec, stream_handle: int
                                      ctypes.c_void_p(stream_handle))
         if rc != 0:
             raise RuntimeError(f"synth_fill_tensor(tensor {t}) returned {rc}")
+
+
+def stream_read(ptr: int, nbytes: int, blocks: int, sink_ptr: int, stream_handle: int = 0) -> None:
+    """The bench's read-bandwidth calibration: a plain streaming read of
+    nbytes at device address ``ptr`` (not part of the method)."""
+    rc = lib().synth_stream_read(ctypes.c_void_p(ptr), nbytes, blocks, ctypes.c_void_p(sink_ptr),
+                                 ctypes.c_void_p(stream_handle))
+    if rc != 0:
+        raise RuntimeError(f"synth_stream_read returned {rc}")

@@ -63,9 +63,43 @@ __global__ void fill_kernel(uint8_t* base, int64_t stride, int64_t offset,
   }
 }
 
+// The bench's read-bandwidth calibration (not part of the method): every
+// thread reads 16-byte words of [p, p + n16 * 16) with non-temporal loads, in
+// a grid-stride walk (consecutive lanes, consecutive words), and folds them
+// into one word per workgroup so that no load can be dropped.
+__global__ __launch_bounds__(256) void read_kernel(const uint4* p, int64_t n16, uint32_t* sink) {
+  uint32_t acc = 0;
+  const int64_t step = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += step) {
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + i));
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  __shared__ uint32_t red[256];
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t a = 0;
+    for (int t = 0; t < 256; ++t) a ^= red[t];
+    sink[blockIdx.x] = a;
+  }
+}
+
 }  // namespace
 
 extern "C" {
+
+// Streaming read of nbytes (a multiple of 16, 16-byte aligned) at device
+// address p with `blocks` workgroups of 256 threads; sink holds `blocks`
+// words.  Returns 0 or the HIP error code of the launch.
+int synth_stream_read(const void* p, int64_t nbytes, int32_t blocks, uint32_t* sink, void* stream) {
+  if (!p || !sink || nbytes <= 0 || nbytes % 16 || (uintptr_t)p % 16 || blocks < 1) return -1;
+  hipLaunchKernelGGL(read_kernel, dim3((unsigned)blocks), dim3(256), 0,
+                     reinterpret_cast<hipStream_t>(stream), static_cast<const uint4*>(p),
+                     nbytes / 16, sink);
+  hipError_t err = hipGetLastError();
+  return err == hipSuccess ? 0 : (int)err;
+}
 
 // Fill tensor `tensor` (0..6, the ids of synth/__init__.py) of experts
 // [0, num_experts) of a bank at `base` (device memory): expert e's tensor starts

@@ -505,6 +505,33 @@ def test_batched_expert_fwd_invalid_and_repeated_slots():
     assert_close(got[:4], ref[:4], "batched expert_fwd")
 
 
+@pytest.mark.parametrize("ties", [448, 70])
+def test_decode_kernel_clustered_winners(ties):
+    """The one-launch decode kernel (W50 shape, top-16) when more than 64
+    experts share the threshold: the first `ties` router rows are identical,
+    so their logits tie exactly above all others (the rest are scaled down),
+    and the top 16 are the tied experts of lowest index.  Selection
+    bit-exact with the oracle, output within the bar."""
+    wl = synth.WORKLOADS["w50_k16"]
+    say(f"[decode] clustered winners: {ties} tied logits")
+    spec = wl.bank(0)
+    bank = cached_bank(spec)
+    Wr, x = synth.layer_inputs(wl, 0, C=1)
+    Wr = Wr.copy()
+    row = np.abs(Wr[0]) * np.sign(x[0])          # a row with a large positive logit
+    Wr[:ties] = row
+    Wr[ties:] *= 0.01
+    out = torch.empty((1, wl.H), dtype=torch.float32, device="cuda")
+    idx = torch.empty((1, wl.k), dtype=torch.int32, device="cuda")
+    rf().moe_layer_fwd(bank, to_dev(Wr), to_dev(x), 1, wl.k, out, idx, None,
+                       _ws(wl.E, wl.H, wl.I, wl.k, 1))
+    torch.cuda.synchronize()
+    ref = oracle.layer(spec, Wr, x, wl.k)
+    assert ref["idx"][0].tolist() == list(range(wl.k))
+    assert np.array_equal(idx.cpu().numpy(), ref["idx"])
+    assert_close(out.cpu().numpy(), ref["out"], f"clustered winners ({ties} ties)")
+
+
 def test_decode_expert_fwd_invalid_and_repeated_slots():
     """The one-launch decode kernel with a caller selection (W50 shape, top-16):
     an invalid slot contributes nothing and a repeated expert counts twice."""
