@@ -43,6 +43,8 @@
 //   k_btopk     one wave per token: the same exact top-k as the decode path
 #include "common.h"
 
+#include <atomic>
+
 namespace rf4 {
 namespace {
 
@@ -875,14 +877,14 @@ constexpr int bdma_lds_bytes() {
 template <int FMT, bool GU, int RM>
 moe_status launch_bdma(const BArgs& a, dim3 grid, hipStream_t st) {
   constexpr int bytes = bdma_lds_bytes<FMT, GU, RM>();
-  static bool attr_set[64] = {false};
+  static std::atomic<bool> attr_set[64];   // per device, set once (concurrent setters agree)
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  if (!attr_set[dev]) {
+  if (!attr_set[dev].load(std::memory_order_relaxed)) {
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(k_bdma<FMT, GU, RM>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, bytes) != hipSuccess)
       return MOE_ERR_DEVICE;
-    attr_set[dev] = true;
+    attr_set[dev].store(true, std::memory_order_relaxed);
   }
   hipLaunchKernelGGL((k_bdma<FMT, GU, RM>), grid, dim3(256), bytes, st, a);
   return MOE_OK;
@@ -1086,6 +1088,77 @@ __device__ int block_excl_scan_dwg(int v, int* s_w, int* total) {
   return base + incl - v;
 }
 
+// One pass of one distinct expert's rows [rsb, rse) of row steps against NTC
+// staged pairs (nt of them used): the gate/up rows with SwiGLU into h, or the
+// down rows times the routing weight into part.  NTC is a compile-time count
+// so that no activation of an unused pair slot is read: the kernel picks the
+// smallest instance that holds the pass.
+template <int FMT, bool GU, int NTC>
+__device__ __forceinline__ void dstream_pass(const DArgs& a, const uint8_t* rec, int rsb, int rse,
+                                             const float* xs, int ts, int nt, const int* s_pairs) {
+  const int H = a.H, I = a.I, K = GU ? H : I;
+  const int B = (FMT == MOE_FMT_MXFP4) ? 32 : 16;
+  constexpr int RS = GU ? kDGrp : 2 * kDGrp;          // rows per row step
+  const int kch = K / 512;                            // 256-byte chunks per row
+  const int grp = threadIdx.x >> 4, l16 = threadIdx.x & 15;
+  const uint32_t rowb = (uint32_t)(K / 2), srowb = (uint32_t)(K / B);
+  constexpr int NT = NTC;
+  const int rows = rse - rsb;
+  if (GU) {
+    __amdgpu_buffer_rsrc_t crs[2], srs[2];
+    crs[0] = view(rec + a.off[MOE_T_GATE_CODES], (uint32_t)I * rowb);
+    crs[1] = view(rec + a.off[MOE_T_UP_CODES], (uint32_t)I * rowb);
+    srs[0] = view(rec + a.off[MOE_T_GATE_SCALES], (uint32_t)I * srowb);
+    srs[1] = view(rec + a.off[MOE_T_UP_SCALES], (uint32_t)I * srowb);
+    const int row0 = rsb * RS + grp;
+    const uint32_t coff[2] = {(uint32_t)row0 * rowb + l16 * 16, (uint32_t)row0 * rowb + l16 * 16};
+    const uint32_t soff[2] = {(uint32_t)row0 * srowb + l16 * (32 / B), (uint32_t)row0 * srowb + l16 * (32 / B)};
+    float gg = 1.0f, gu = 1.0f;
+    if (FMT == MOE_FMT_NVFP4) {
+      const float* gl = reinterpret_cast<const float*>(rec + a.off[MOE_T_GLOBALS]);
+      gg = gl[0];
+      gu = gl[1];
+    }
+    dstream_rows<FMT, 2, NT>(crs, srs, coff, soff, RS * rowb, RS * srowb, rows, kch, xs, ts, nt,
+                             [&](int ri, float (&acc)[2][NT]) {
+      const int j = row0 + ri * RS;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        if (t >= nt) break;
+        const float gs = group16_sum(acc[0][t]);
+        const float us = group16_sum(acc[1][t]);
+        if (l16 == 0) a.h[(size_t)s_pairs[t] * I + j] = silu(gg * gs) * (gu * us);
+      }
+    });
+  } else {
+    __amdgpu_buffer_rsrc_t crs[2], srs[2];
+    crs[0] = crs[1] = view(rec + a.off[MOE_T_DOWN_CODES], (uint32_t)H * rowb);
+    srs[0] = srs[1] = view(rec + a.off[MOE_T_DOWN_SCALES], (uint32_t)H * srowb);
+    const int row0 = rsb * RS + grp;                // and row0 + kDGrp
+    const uint32_t coff[2] = {(uint32_t)row0 * rowb + l16 * 16, (uint32_t)(row0 + kDGrp) * rowb + l16 * 16};
+    const uint32_t soff[2] = {(uint32_t)row0 * srowb + l16 * (32 / B),
+                              (uint32_t)(row0 + kDGrp) * srowb + l16 * (32 / B)};
+    float gd = 1.0f;
+    if (FMT == MOE_FMT_NVFP4) gd = reinterpret_cast<const float*>(rec + a.off[MOE_T_GLOBALS])[2];
+    dstream_rows<FMT, 2, NT>(crs, srs, coff, soff, RS * rowb, RS * srowb, rows, kch, xs, ts, nt,
+                             [&](int ri, float (&acc)[2][NT]) {
+      const int j = row0 + ri * RS;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        if (t >= nt) break;
+        const int p = s_pairs[t];
+        const float wp = a.w[p] * gd;
+        const float y0 = group16_sum(acc[0][t]);
+        const float y1 = group16_sum(acc[1][t]);
+        if (l16 == 0) {
+          a.part[(size_t)p * H + j] = wp * y0;
+          a.part[(size_t)p * H + j + kDGrp] = wp * y1;
+        }
+      }
+    });
+  }
+}
+
 template <int FMT, bool GU, int NT>
 __global__ __launch_bounds__(kDWG) void k_dstream(DArgs a) {
   extern __shared__ __attribute__((aligned(16))) float xs[];   // [ntp][K / 32 * 36]
@@ -1097,10 +1170,8 @@ __global__ __launch_bounds__(kDWG) void k_dstream(DArgs a) {
   const int CK = a.C * a.k;
   const int nu = a.disp[0];
   const int H = a.H, I = a.I, K = GU ? H : I, N = GU ? I : H;
-  const int B = (FMT == MOE_FMT_MXFP4) ? 32 : 16;
   constexpr int RS = GU ? kDGrp : 2 * kDGrp;          // rows per row step
   const int nrs = N / RS;
-  const int kch = K / 512;                            // 256-byte chunks per row
   const int ts = K / 32 * 36;                         // LDS floats per staged pair
   const int ntp = a.ntp;
 
@@ -1127,8 +1198,6 @@ __global__ __launch_bounds__(kDWG) void k_dstream(DArgs a) {
   __syncthreads();
   const int g0 = s_bound[0], g1 = s_bound[1];
 
-  const int grp = tid >> 4, l16 = tid & 15;
-  const uint32_t rowb = (uint32_t)(K / 2), srowb = (uint32_t)(K / B);
   for (int u = g0 / nrs; u * nrs < g1; ++u) {
     const int rsb = max(g0 - u * nrs, 0), rse = min(g1 - u * nrs, nrs);
     if (rsb >= rse) continue;
@@ -1148,74 +1217,25 @@ __global__ __launch_bounds__(kDWG) void k_dstream(DArgs a) {
         *reinterpret_cast<float4*>(xs + t * ts + kk + (kk >> 5) * 4) = v;
       }
       __syncthreads();
-      const int rows = rse - rsb;
-      if (GU) {
-        __amdgpu_buffer_rsrc_t crs[2], srs[2];
-        crs[0] = view(rec + a.off[MOE_T_GATE_CODES], (uint32_t)I * rowb);
-        crs[1] = view(rec + a.off[MOE_T_UP_CODES], (uint32_t)I * rowb);
-        srs[0] = view(rec + a.off[MOE_T_GATE_SCALES], (uint32_t)I * srowb);
-        srs[1] = view(rec + a.off[MOE_T_UP_SCALES], (uint32_t)I * srowb);
-        const int row0 = rsb * RS + grp;
-        const uint32_t coff[2] = {(uint32_t)row0 * rowb + l16 * 16, (uint32_t)row0 * rowb + l16 * 16};
-        const uint32_t soff[2] = {(uint32_t)row0 * srowb + l16 * (32 / B), (uint32_t)row0 * srowb + l16 * (32 / B)};
-        float gg = 1.0f, gu = 1.0f;
-        if (FMT == MOE_FMT_NVFP4) {
-          const float* gl = reinterpret_cast<const float*>(rec + a.off[MOE_T_GLOBALS]);
-          gg = gl[0];
-          gu = gl[1];
-        }
-        dstream_rows<FMT, 2, NT>(crs, srs, coff, soff, RS * rowb, RS * srowb, rows, kch, xs, ts, nt,
-                                 [&](int ri, float (&acc)[2][NT]) {
-          const int j = row0 + ri * RS;
-#pragma unroll
-          for (int t = 0; t < NT; ++t) {
-            if (t >= nt) break;
-            const float gs = group16_sum(acc[0][t]);
-            const float us = group16_sum(acc[1][t]);
-            if (l16 == 0) a.h[(size_t)s_pairs[t] * I + j] = silu(gg * gs) * (gu * us);
-          }
-        });
-      } else {
-        __amdgpu_buffer_rsrc_t crs[2], srs[2];
-        crs[0] = crs[1] = view(rec + a.off[MOE_T_DOWN_CODES], (uint32_t)H * rowb);
-        srs[0] = srs[1] = view(rec + a.off[MOE_T_DOWN_SCALES], (uint32_t)H * srowb);
-        const int row0 = rsb * RS + grp;                // and row0 + kDGrp
-        const uint32_t coff[2] = {(uint32_t)row0 * rowb + l16 * 16, (uint32_t)(row0 + kDGrp) * rowb + l16 * 16};
-        const uint32_t soff[2] = {(uint32_t)row0 * srowb + l16 * (32 / B),
-                                  (uint32_t)(row0 + kDGrp) * srowb + l16 * (32 / B)};
-        float gd = 1.0f;
-        if (FMT == MOE_FMT_NVFP4) gd = reinterpret_cast<const float*>(rec + a.off[MOE_T_GLOBALS])[2];
-        dstream_rows<FMT, 2, NT>(crs, srs, coff, soff, RS * rowb, RS * srowb, rows, kch, xs, ts, nt,
-                                 [&](int ri, float (&acc)[2][NT]) {
-          const int j = row0 + ri * RS;
-#pragma unroll
-          for (int t = 0; t < NT; ++t) {
-            if (t >= nt) break;
-            const int p = s_pairs[t];
-            const float wp = a.w[p] * gd;
-            const float y0 = group16_sum(acc[0][t]);
-            const float y1 = group16_sum(acc[1][t]);
-            if (l16 == 0) {
-              a.part[(size_t)p * H + j] = wp * y0;
-              a.part[(size_t)p * H + j + kDGrp] = wp * y1;
-            }
-          }
-        });
-      }
+      // a pass of one pair runs the one-pair instance, so that no unused pair
+      // slot's activations are read; others the workgroup's own
+      if (NT == 1 || nt == 1) dstream_pass<FMT, GU, 1>(a, rec, rsb, rse, xs, ts, 1, s_pairs);
+      else if (NT == 2 || nt == 2) dstream_pass<FMT, GU, 2>(a, rec, rsb, rse, xs, ts, 2, s_pairs);
+      else dstream_pass<FMT, GU, NT>(a, rec, rsb, rse, xs, ts, nt, s_pairs);
     }
   }
 }
 
 template <int FMT, bool GU, int NT>
 moe_status launch_dstream_nt(const DArgs& a, int grid, int lds, hipStream_t st) {
-  static bool attr_set[64] = {false};
+  static std::atomic<bool> attr_set[64];   // per device, set once (concurrent setters agree)
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  if (!attr_set[dev]) {
+  if (!attr_set[dev].load(std::memory_order_relaxed)) {
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(k_dstream<FMT, GU, NT>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, kDLds) != hipSuccess)
       return MOE_ERR_DEVICE;
-    attr_set[dev] = true;
+    attr_set[dev].store(true, std::memory_order_relaxed);
   }
   hipLaunchKernelGGL((k_dstream<FMT, GU, NT>), dim3(grid), dim3(kDWG), lds, st, a);
   return MOE_OK;
@@ -1244,16 +1264,16 @@ int dstream_ntp(int K) {
 
 // Workgroups of the decode-batch streams: one per compute unit.
 int dstream_grid() {
-  static int cache[64] = {0};
+  static std::atomic<int> cache[64];   // per device, 0 until first asked
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cache[dev] == 0) {
-    int n = 0;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
       n = 256;
-    cache[dev] = n;
+    cache[dev].store(n, std::memory_order_relaxed);
   }
-  return cache[dev];
+  return n;
 }
 
 moe_status status_of_launch() { return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_DEVICE; }
