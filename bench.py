@@ -85,7 +85,8 @@ def calibrate_copy():
 def read_bandwidth(window_bytes: int = 323_018_944, total_gib: int = 16, passes: int = 4):
     """The achievable HBM read rate on this GPU, measured with a plain
     streaming read (synth.device.stream_read: 16-byte non-temporal loads,
-    2048 workgroups of 256 threads, grid-stride):
+    four in flight per thread, grid-stride), the best of 1024, 2048 and 4096
+    workgroups of 256 threads:
 
     * streaming: the whole 16 GiB buffer (64x the 256 MB last-level cache)
       per launch, best of `passes`;
@@ -99,29 +100,28 @@ def read_bandwidth(window_bytes: int = 323_018_944, total_gib: int = 16, passes:
     import synth.device as sd
     n = total_gib << 30
     buf = torch.empty(n, dtype=torch.uint8, device="cuda")
-    blocks = 2048
-    sink = torch.empty(blocks, dtype=torch.int32, device="cuda")
+    sink = torch.empty(4096, dtype=torch.int32, device="cuda")
     st = torch.cuda.current_stream()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    sd.stream_read(buf.data_ptr(), n, blocks, sink.data_ptr(), st.cuda_stream)     # warm-up
-    best = 0.0
-    for _ in range(passes):
-        a.record(st)
-        sd.stream_read(buf.data_ptr(), n, blocks, sink.data_ptr(), st.cuda_stream)
-        b.record(st)
-        torch.cuda.synchronize()
-        best = max(best, n / (a.elapsed_time(b) * 1e-3) / 1e9)
     w = (window_bytes + 4095) // 4096 * 4096
     nwin = n // w
-    launches = 200
-    a.record(st)
-    for i in range(launches):
-        off = (i % nwin) * w
-        sd.stream_read(buf.data_ptr() + off, window_bytes // 16 * 16, blocks, sink.data_ptr(),
-                       st.cuda_stream)
-    b.record(st)
-    torch.cuda.synchronize()
-    single = window_bytes // 16 * 16 * launches / (a.elapsed_time(b) * 1e-3) / 1e9
+    nb = window_bytes // 16 * 16
+    best, single = 0.0, 0.0
+    for blocks in (1024, 2048, 4096):
+        sd.stream_read(buf.data_ptr(), n, blocks, sink.data_ptr(), st.cuda_stream)     # warm-up
+        for _ in range(passes):
+            a.record(st)
+            sd.stream_read(buf.data_ptr(), n, blocks, sink.data_ptr(), st.cuda_stream)
+            b.record(st)
+            torch.cuda.synchronize()
+            best = max(best, n / (a.elapsed_time(b) * 1e-3) / 1e9)
+        launches = 100
+        a.record(st)
+        for i in range(launches):
+            sd.stream_read(buf.data_ptr() + (i % nwin) * w, nb, blocks, sink.data_ptr(), st.cuda_stream)
+        b.record(st)
+        torch.cuda.synchronize()
+        single = max(single, nb * launches / (a.elapsed_time(b) * 1e-3) / 1e9)
     del buf
     torch.cuda.empty_cache()
     return best, single

@@ -65,13 +65,22 @@ __global__ void fill_kernel(uint8_t* base, int64_t stride, int64_t offset,
 
 // The bench's read-bandwidth calibration (not part of the method): every
 // thread reads 16-byte words of [p, p + n16 * 16) with non-temporal loads, in
-// a grid-stride walk (consecutive lanes, consecutive words), and folds them
-// into one word per workgroup so that no load can be dropped.
+// a grid-stride walk (consecutive lanes, consecutive words; four words in
+// flight per thread), and folds them into one word per workgroup so that no
+// load can be dropped.
 __global__ __launch_bounds__(256) void read_kernel(const uint4* p, int64_t n16, uint32_t* sink) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
   uint32_t acc = 0;
   const int64_t step = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += step) {
-    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (; i + 3 * step < n16; i += 4 * step) {
+    u32x4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + i + u * step));
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  for (; i < n16; i += step) {
     const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + i));
     acc ^= v.x ^ v.y ^ v.z ^ v.w;
   }
