@@ -348,12 +348,13 @@ def bench_latent(args, wl):
     fmt = "nvfp4" if wl.fmt == synth.FMT_NV else "mxfp4"
     if C == 1:
         kernels = ("k_gemv (routed_down, with the shared selection), k_moe1 (router on the hidden "
-                   "state + routed experts, one launch), shared experts (k_dispatch + "
-                   "k_dstream<GU> + k_dstream<DN> + k_bcombine), k_gemv (norm + routed_up)")
+                   "state + routed experts, one launch), shared experts (k_sgu + k_sdn), "
+                   "k_gemv (norm + routed_up)")
     else:
-        kernels = ("k_gemv (routed_down, with the shared selection), k_route + k_btopk (router), "
-                   "routed experts and then shared experts (k_dispatch + k_dstream<GU> + "
-                   "k_dstream<DN> + k_bcombine each), k_gemv (norm + routed_up)")
+        kernels = ("k_gemv (routed_down, with the shared selection and dispatch table), "
+                   "k_route + k_btopk (router and routed dispatch table), routed experts and "
+                   "then shared experts (k_dstream<GU> + k_dstream<DN> + k_bcombine each), "
+                   "k_gemv (norm + routed_up)")
     result = {
         "metric": "latent MoE layer decode µs/token + achieved HBM GB/s (% of peak)",
         "value": round(us_call / C, 3),

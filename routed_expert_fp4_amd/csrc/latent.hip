@@ -22,9 +22,13 @@
 //               1 / rms(x[t]), else s_t = 1 and g = 1.  The routed_down launch
 //               also writes the shared experts' selection (every token, every
 //               shared expert, weight 1).
-//   k_sgu, k_sdn the shared experts for one token: gate/up with SwiGLU, then
-//               down summed over the shared experts, as row-blocked mat-vecs
-//               (more tokens take the library's decode-batch streams)
+//   k_lat_in    one token: routed_down (as k_gemv) and, in the same launch,
+//               the shared experts' gate/up with SwiGLU as row-blocked
+//               mat-vecs (both read only x)
+//   k_lat_out   one token: per block of 8 output rows, the shared experts'
+//               down sum plus routed_up with the norm folded in
+//   (more tokens: k_gemv for the dense steps and the library's decode-batch
+//   streams for the shared experts)
 #include "common.h"
 
 namespace rf4 {
@@ -46,6 +50,15 @@ struct GemvArgs {
 
 constexpr int kGemvWG = 256;
 
+// Weight bytes are read once per call: non-temporal loads keep them from
+// displacing the activations in the caches (1 to 1.5 us per launch on the
+// K3 latent shape against plain loads).
+typedef unsigned int nt_u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_nt16(const uint8_t* p) {
+  const nt_u32x4_t t = __builtin_nontemporal_load(reinterpret_cast<const nt_u32x4_t*>(p));
+  return make_uint4(t.x, t.y, t.z, t.w);
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
@@ -66,44 +79,42 @@ __device__ __forceinline__ float wave_sum_dpp(float v) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
-// RB rows per workgroup, the whole K: the 256 threads split each row into
-// 16-byte chunks (8 bf16), NCH chunks per thread per slab of 2048 * NCH
-// elements; every weight load of a slab is issued before any arithmetic, and x
-// (with gamma applied) comes straight from L2 into registers for each chunk, in
-// groups of up to 4 tokens.  With the norm, the same x values give each
-// token's sum of squares over K.  The per-thread partial sums are reduced over
-// the wave (DPP) and then over the four waves in order.
-template <int RB, int CM, int NCH>
-__global__ __launch_bounds__(kGemvWG) void k_gemv(GemvArgs a) {
-  constexpr int TG = CM < 4 ? CM : 4;                 // tokens per x group
-  __shared__ float s_part[kGemvWG / 64][RB * CM + CM];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int C = a.C, K = a.K, N = a.N, K8 = K >> 3;
-  const int n0 = blockIdx.x * RB;
-  const bool norm = a.gamma != nullptr;
-
-  if (a.sel_idx && blockIdx.x == 0) {
-    const int ns = a.ns, CK = C * ns;
-    for (int i = tid; i < CK; i += kGemvWG) {
-      a.sel_idx[i] = i % ns;
-      a.sel_w[i] = 1.0f;
+// The shared experts' selection (every token, every shared expert, weight 1)
+// and, where asked for, their dispatch table: distinct experts in order of
+// first use (0 .. ns-1), each with every token's pair t * ns + u in token
+// order.  Block 0 of the routed_down launch writes them.
+__device__ void write_shared_selection(const GemvArgs& a) {
+  const int tid = threadIdx.x, ns = a.ns, C = a.C, CK = C * ns;
+  for (int i = tid; i < CK; i += kGemvWG) {
+    a.sel_idx[i] = i % ns;
+    a.sel_w[i] = 1.0f;
+  }
+  if (a.sel_disp) {
+    if (tid == 0) a.sel_disp[0] = ns;
+    for (int u = tid; u < ns; u += kGemvWG) {
+      a.sel_disp[disp_uexp(CK) + u] = u;
+      a.sel_disp[disp_untok(CK) + u] = C;
     }
-    if (a.sel_disp) {
-      // distinct experts in order of first use (0 .. ns-1), each with every
-      // token's pair t * ns + u in token order
-      if (tid == 0) a.sel_disp[0] = ns;
-      for (int u = tid; u < ns; u += kGemvWG) {
-        a.sel_disp[disp_uexp(CK) + u] = u;
-        a.sel_disp[disp_untok(CK) + u] = C;
-      }
-      for (int i = tid; i < CK; i += kGemvWG) {
-        const int u = i / C, t = i - u * C;
-        a.sel_disp[disp_upair(CK) + u * C + t] = t * ns + u;
-      }
+    for (int i = tid; i < CK; i += kGemvWG) {
+      const int u = i / C, t = i - u * C;
+      a.sel_disp[disp_upair(CK) + u * C + t] = t * ns + u;
     }
   }
+}
 
-  float acc[RB][CM], ss[CM];
+// Rows n0 .. n0+RB-1, the whole K, per-thread partial sums: the 256 threads
+// split each row into 16-byte chunks (8 bf16), NCH chunks per thread per slab
+// of 2048 * NCH elements; every weight load of a slab is issued before any
+// arithmetic, and x (with gamma applied) comes straight from L2 into
+// registers for each chunk, in groups of up to 4 tokens.  With the norm, the
+// same x values give each token's sum of squares over K (ss).
+template <int RB, int CM, int NCH>
+__device__ __forceinline__ void gemv_dot(const GemvArgs& a, int n0, float (&acc)[RB][CM],
+                                         float (&ss)[CM]) {
+  constexpr int TG = CM < 4 ? CM : 4;                 // tokens per x group
+  const int tid = threadIdx.x;
+  const int C = a.C, K = a.K, N = a.N, K8 = K >> 3;
+  const bool norm = a.gamma != nullptr;
 #pragma unroll
   for (int t = 0; t < CM; ++t) {
     ss[t] = 0.0f;
@@ -120,7 +131,7 @@ __global__ __launch_bounds__(kGemvWG) void k_gemv(GemvArgs a) {
       for (int r = 0; r < RB; ++r) {
         const int n = n0 + r;
         wq[r][j] = (c < K8 && n < N)
-                       ? reinterpret_cast<const uint4*>(a.W + (size_t)n * K)[c]
+                       ? load_nt16(reinterpret_cast<const uint8_t*>(a.W + (size_t)n * K) + 16 * c)
                        : make_uint4(0u, 0u, 0u, 0u);
       }
     }
@@ -169,6 +180,22 @@ __global__ __launch_bounds__(kGemvWG) void k_gemv(GemvArgs a) {
       }
     }
   }
+}
+
+// Block blk of the mat-vec: rows blk*RB .. blk*RB+RB-1.  The per-thread
+// partial sums are reduced over the wave (DPP) and then over the four waves
+// in order.
+template <int RB, int CM, int NCH>
+__device__ __forceinline__ void gemv_block(const GemvArgs& a, int blk) {
+  __shared__ float s_part[kGemvWG / 64][RB * CM + CM];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int C = a.C, K = a.K, N = a.N;
+  const int n0 = blk * RB;
+  const bool norm = a.gamma != nullptr;
+  if (a.sel_idx && blk == 0) write_shared_selection(a);
+
+  float acc[RB][CM], ss[CM];
+  gemv_dot<RB, CM, NCH>(a, n0, acc, ss);
 
 #pragma unroll
   for (int t = 0; t < CM; ++t) {
@@ -202,6 +229,11 @@ __global__ __launch_bounds__(kGemvWG) void k_gemv(GemvArgs a) {
 }
 
 template <int RB, int CM, int NCH>
+__global__ __launch_bounds__(kGemvWG) void k_gemv(GemvArgs a) {
+  gemv_block<RB, CM, NCH>(a, blockIdx.x);
+}
+
+template <int RB, int CM, int NCH>
 void launch_gemv_t(const GemvArgs& a, hipStream_t st) {
   const int grid = (a.N + RB - 1) / RB;
   hipLaunchKernelGGL((k_gemv<RB, CM, NCH>), dim3(grid), dim3(kGemvWG), 0, st, a);
@@ -215,9 +247,9 @@ moe_status launch_gemv(const GemvArgs& a, hipStream_t st) {
 }
 
 // ---------------------------------------------------------------------------
-// Shared experts for one token: every shared expert, weight 1, as two
-// row-blocked mat-vec launches (the decode-batch streams, built for many
-// experts, leave most CUs idle on two).
+// Shared experts for one token: every shared expert, weight 1, as row-blocked
+// mat-vecs folded into the two dense launches (the decode-batch streams,
+// built for many experts, leave most CUs idle on two).
 // ---------------------------------------------------------------------------
 struct SArgs {
   const uint8_t* base;
@@ -226,7 +258,6 @@ struct SArgs {
   int ns, H, I;
   const float* x;   // [H]
   float* h;         // [ns][I]
-  float* out;       // [H]
 };
 
 constexpr int kSRowsGU = 4;      // intermediate rows (gate and up) per workgroup
@@ -261,8 +292,8 @@ __device__ __forceinline__ float sdot32(const uint4& q, uint32_t sc, const float
 
 template <int FMT>
 __device__ __forceinline__ uint32_t sscale(const uint8_t* srow, int c) {
-  if (FMT == MOE_FMT_MXFP4) return srow[c];
-  return *reinterpret_cast<const uint16_t*>(srow + 2 * c);
+  if (FMT == MOE_FMT_MXFP4) return __builtin_nontemporal_load(srow + c);
+  return __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(srow + 2 * c));
 }
 
 // gate and up rows i0 .. i0+3 of shared expert blockIdx.y: the 256 threads
@@ -270,11 +301,11 @@ __device__ __forceinline__ uint32_t sscale(const uint8_t* srow, int c) {
 // issued first, sums are reduced over the wave (DPP) and the four waves in
 // order; h = silu(g) * u.
 template <int FMT>
-__global__ __launch_bounds__(256) void k_sgu(SArgs a) {
+__device__ __forceinline__ void sgu_block(const SArgs& a, int j, int i0) {
   constexpr int B = FMT == MOE_FMT_MXFP4 ? 32 : 16;
   __shared__ float s_part[4][2 * kSRowsGU];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int j = blockIdx.y, i0 = blockIdx.x * kSRowsGU, H = a.H, nch = H / 32;
+  const int H = a.H, nch = H / 32;
   const uint8_t* rec = a.base + (size_t)j * a.stride;
   const uint8_t* cb[2] = {rec + a.off[MOE_T_GATE_CODES], rec + a.off[MOE_T_UP_CODES]};
   const uint8_t* sbp[2] = {rec + a.off[MOE_T_GATE_SCALES], rec + a.off[MOE_T_UP_SCALES]};
@@ -289,7 +320,7 @@ __global__ __launch_bounds__(256) void k_sgu(SArgs a) {
       for (int m = 0; m < 2; ++m) {
         if (c < nch) {
           const size_t row = (size_t)(i0 + r);
-          q[u][r][m] = *reinterpret_cast<const uint4*>(cb[m] + row * (H / 2) + 16 * c);
+          q[u][r][m] = load_nt16(cb[m] + row * (H / 2) + 16 * c);
           sc[u][r][m] = sscale<FMT>(sbp[m] + row * (H / B), c);
         } else {
           q[u][r][m] = make_uint4(0u, 0u, 0u, 0u);
@@ -338,36 +369,43 @@ __global__ __launch_bounds__(256) void k_sgu(SArgs a) {
   }
 }
 
-// out rows n0 .. n0+7 = sum over shared experts of W_down h: the threads
-// split the concatenated K (every expert's I) into 32-element chunks.
-template <int FMT>
-__global__ __launch_bounds__(256) void k_sdn(SArgs a) {
+// Shared-expert down rows n0 .. n0+RD-1: the threads split the concatenated
+// K (every shared expert's I) into 32-element chunks; sdn_load issues the
+// weight loads, sdn_dot the per-thread partial sums.
+template <int RD>
+struct SdnW {
+  uint4 q[kSMaxCh][RD];
+  uint32_t sc[kSMaxCh][RD];
+};
+
+template <int FMT, int RD>
+__device__ __forceinline__ void sdn_load(const SArgs& a, int n0, SdnW<RD>& w) {
   constexpr int B = FMT == MOE_FMT_MXFP4 ? 32 : 16;
-  __shared__ float s_part[4][kSRowsDN];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int n0 = blockIdx.x * kSRowsDN, I = a.I, nchI = I / 32, ntot = a.ns * nchI;
-  uint4 q[kSMaxCh][kSRowsDN];
-  uint32_t sc[kSMaxCh][kSRowsDN];
+  const int tid = threadIdx.x, I = a.I, nchI = I / 32, ntot = a.ns * nchI;
 #pragma unroll
   for (int u = 0; u < kSMaxCh; ++u) {
     const int cc = tid + 256 * u;
     const int j = cc < ntot ? cc / nchI : 0, c = cc < ntot ? cc - j * nchI : 0;
     const uint8_t* rec = a.base + (size_t)j * a.stride;
 #pragma unroll
-    for (int r = 0; r < kSRowsDN; ++r) {
+    for (int r = 0; r < RD; ++r) {
       if (cc < ntot) {
         const size_t row = (size_t)(n0 + r);
-        q[u][r] = *reinterpret_cast<const uint4*>(rec + a.off[MOE_T_DOWN_CODES] + row * (I / 2) + 16 * c);
-        sc[u][r] = sscale<FMT>(rec + a.off[MOE_T_DOWN_SCALES] + row * (I / B), c);
+        w.q[u][r] = load_nt16(rec + a.off[MOE_T_DOWN_CODES] + row * (I / 2) + 16 * c);
+        w.sc[u][r] = sscale<FMT>(rec + a.off[MOE_T_DOWN_SCALES] + row * (I / B), c);
       } else {
-        q[u][r] = make_uint4(0u, 0u, 0u, 0u);
-        sc[u][r] = 0u;
+        w.q[u][r] = make_uint4(0u, 0u, 0u, 0u);
+        w.sc[u][r] = 0u;
       }
     }
   }
-  float acc[kSRowsDN];
+}
+
+template <int FMT, int RD>
+__device__ __forceinline__ void sdn_dot(const SArgs& a, const SdnW<RD>& w, float (&acc)[RD]) {
+  const int tid = threadIdx.x, I = a.I, nchI = I / 32, ntot = a.ns * nchI;
 #pragma unroll
-  for (int r = 0; r < kSRowsDN; ++r) acc[r] = 0.0f;
+  for (int r = 0; r < RD; ++r) acc[r] = 0.0f;
 #pragma unroll
   for (int u = 0; u < kSMaxCh; ++u) {
     const int cc = tid + 256 * u;
@@ -384,17 +422,67 @@ __global__ __launch_bounds__(256) void k_sdn(SArgs a) {
         hv[4 * v] = f.x; hv[4 * v + 1] = f.y; hv[4 * v + 2] = f.z; hv[4 * v + 3] = f.w;
       }
 #pragma unroll
-      for (int r = 0; r < kSRowsDN; ++r) acc[r] += g * sdot32<FMT>(q[u][r], sc[u][r], hv);
+      for (int r = 0; r < RD; ++r) acc[r] += g * sdot32<FMT>(w.q[u][r], w.sc[u][r], hv);
     }
   }
-#pragma unroll
-  for (int r = 0; r < kSRowsDN; ++r) {
-    const float v = wave_sum_dpp(acc[r]);
-    if (lane == 0) s_part[wave][r] = v;
+}
+
+// ---------------------------------------------------------------------------
+// One token: the dense mat-vecs and the shared experts in two launches.
+// ---------------------------------------------------------------------------
+// First: x_lat = W_down x (blocks 0 .. nA-1, kLatRowsA rows each) and the
+// shared experts' gate/up with SwiGLU (the other blocks, kSRowsGU rows of one
+// expert each).  Both read only x, so one launch streams both weight sets.
+constexpr int kLatRowsA = 8;
+
+template <int FMT>
+__global__ __launch_bounds__(256) void k_lat_in(GemvArgs g, SArgs s, int nA) {
+  const int b = blockIdx.x;
+  if (b < nA) {
+    gemv_block<kLatRowsA, 1, 4>(g, b);
+  } else {
+    const int per = s.I / kSRowsGU, q = b - nA;
+    sgu_block<FMT>(s, q / per, (q - (q / per) * per) * kSRowsGU);
   }
+}
+
+// Last: out rows n0 .. n0+7 = (sum over the shared experts of W_down h) +
+// W_up (gamma * y_lat) / rms(y_lat), both in one workgroup: the shared
+// experts' down weights are loaded first, then the W_up rows stream while
+// those loads are in flight.  The sum is formed in the same order as the
+// shared-down launch followed by the accumulating W_up launch.
+template <int FMT>
+__global__ __launch_bounds__(256) void k_lat_out(GemvArgs g, SArgs s) {
+  constexpr int RB = kSRowsDN;
+  __shared__ float s_part[4][2 * RB + 1];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int n0 = blockIdx.x * RB;
+  SdnW<RB> w;
+  sdn_load<FMT, RB>(s, n0, w);
+  float acc[RB][1], ss[1];
+  gemv_dot<RB, 1, 2>(g, n0, acc, ss);
+  float sacc[RB];
+  sdn_dot<FMT, RB>(s, w, sacc);
+#pragma unroll
+  for (int r = 0; r < RB; ++r) {
+    const float v = wave_sum_dpp(acc[r][0]);
+    const float u = wave_sum_dpp(sacc[r]);
+    if (lane == 0) {
+      s_part[wave][r] = v;
+      s_part[wave][RB + r] = u;
+    }
+  }
+  const float q = wave_sum_dpp(ss[0]);
+  if (lane == 0) s_part[wave][2 * RB] = q;
   __syncthreads();
-  if (tid < kSRowsDN)
-    a.out[n0 + tid] = ((s_part[0][tid] + s_part[1][tid]) + s_part[2][tid]) + s_part[3][tid];
+  if (tid < RB) {
+    float v = ((s_part[0][tid] + s_part[1][tid]) + s_part[2][tid]) + s_part[3][tid];
+    const float sq = ((s_part[0][2 * RB] + s_part[1][2 * RB]) + s_part[2][2 * RB]) + s_part[3][2 * RB];
+    v *= 1.0f / sqrtf(sq / (float)g.K + g.eps);
+    const float sh = ((s_part[0][RB + tid] + s_part[1][RB + tid]) + s_part[2][RB + tid]) +
+                     s_part[3][RB + tid];
+    g.y[n0 + tid] = sh + v;
+  }
 }
 
 bool shared1_ok(const moe_bank* S, int H) {
@@ -403,21 +491,34 @@ bool shared1_ok(const moe_bank* S, int H) {
          S->inter % kSRowsGU == 0 && (S->format == MOE_FMT_MXFP4 || S->format == MOE_FMT_NVFP4);
 }
 
-moe_status launch_shared1(const moe_bank* S, const float* x, float* h, float* out, hipStream_t st) {
+SArgs shared_args(const moe_bank* S, const float* x, float* h) {
   SArgs a;
   a.base = static_cast<const uint8_t*>(S->base);
   a.stride = S->expert_stride;
   for (int t = 0; t < MOE_NUM_TENSORS; ++t) a.off[t] = S->offset[t];
   a.ns = S->num_experts; a.H = S->hidden; a.I = S->inter;
-  a.x = x; a.h = h; a.out = out;
-  const dim3 ggu(a.I / kSRowsGU, a.ns), gdn(a.H / kSRowsDN);
-  if (S->format == MOE_FMT_MXFP4) {
-    hipLaunchKernelGGL(k_sgu<MOE_FMT_MXFP4>, ggu, dim3(256), 0, st, a);
-    hipLaunchKernelGGL(k_sdn<MOE_FMT_MXFP4>, gdn, dim3(256), 0, st, a);
-  } else {
-    hipLaunchKernelGGL(k_sgu<MOE_FMT_NVFP4>, ggu, dim3(256), 0, st, a);
-    hipLaunchKernelGGL(k_sdn<MOE_FMT_NVFP4>, gdn, dim3(256), 0, st, a);
-  }
+  a.x = x; a.h = h;
+  return a;
+}
+
+// One token: routed_down (g) and the shared experts' gate/up into h.
+moe_status launch_lat_in(const GemvArgs& g, const SArgs& s, int fmt, hipStream_t st) {
+  const int nA = (g.N + kLatRowsA - 1) / kLatRowsA;
+  const dim3 grid(nA + s.ns * (s.I / kSRowsGU));
+  if (fmt == MOE_FMT_MXFP4)
+    hipLaunchKernelGGL(k_lat_in<MOE_FMT_MXFP4>, grid, dim3(256), 0, st, g, s, nA);
+  else
+    hipLaunchKernelGGL(k_lat_in<MOE_FMT_NVFP4>, grid, dim3(256), 0, st, g, s, nA);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_DEVICE;
+}
+
+// One token: out = shared experts' down sum + routed_up (g, with the norm).
+moe_status launch_lat_out(const GemvArgs& g, const SArgs& s, int fmt, hipStream_t st) {
+  const dim3 grid(g.N / kSRowsDN);
+  if (fmt == MOE_FMT_MXFP4)
+    hipLaunchKernelGGL(k_lat_out<MOE_FMT_MXFP4>, grid, dim3(256), 0, st, g, s);
+  else
+    hipLaunchKernelGGL(k_lat_out<MOE_FMT_NVFP4>, grid, dim3(256), 0, st, g, s);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_DEVICE;
 }
 
@@ -513,7 +614,9 @@ moe_status moe_latent_layer_fwd(const moe_latent_layer* layer, const float* x, i
       !shared_one && bank_status(&S) == MOE_OK && batched_decode_shape(&S, C);
   const WsLayout Ls = ws_layout(ns, S.hidden, S.inter, ns, C);
   g.sel_disp = shared_streams ? reinterpret_cast<int32_t*>(w8 + W.shared + Ls.disp) : nullptr;
-  moe_status s = launch_gemv(g, st);
+  float* sh = reinterpret_cast<float*>(w8 + W.shared + Ls.h);
+  const SArgs sa = shared_args(&S, x, sh);
+  moe_status s = shared_one ? launch_lat_in(g, sa, S.format, st) : launch_gemv(g, st);
   if (s != MOE_OK) return s;
   s = C == 1 ? layer1_router_input(&R, layer->w_router, x, H, xlat, k, ylat, idx, w, wr, wr_bytes, st)
              : MOE_ERR_UNSUPPORTED;
@@ -524,15 +627,15 @@ moe_status moe_latent_layer_fwd(const moe_latent_layer* layer, const float* x, i
     s = moe_expert_fwd(&R, xlat, C, k, idx, w, ylat, wr, wr_bytes, stream);
   }
   if (s != MOE_OK) return s;
-  // finish phase: shared experts into out, then routed_norm and routed_up added
-  s = shared_one ? launch_shared1(&S, x, reinterpret_cast<float*>(w8 + W.shared + Ls.h), out, st)
-      : shared_streams
-          ? launch_batched_decode(&S, x, C, ns, sidx, sw, out, w8 + W.shared, Ls, st)
-          : moe_expert_fwd(&S, x, C, ns, sidx, sw, out, w8 + W.shared, ws_bytes_s, stream);
-  if (s != MOE_OK) return s;
+  // finish phase: shared experts into out, then routed_norm and routed_up
+  // added (one launch for one token)
   g.W = layer->w_up; g.x = ylat; g.gamma = layer->norm_gamma; g.eps = layer->norm_eps; g.y = out;
   g.C = C; g.N = H; g.K = L; g.accumulate = 1;
   g.sel_idx = nullptr; g.sel_w = nullptr; g.sel_disp = nullptr; g.ns = 0;
+  if (shared_one) return launch_lat_out(g, sa, S.format, st);
+  s = shared_streams ? launch_batched_decode(&S, x, C, ns, sidx, sw, out, w8 + W.shared, Ls, st)
+                     : moe_expert_fwd(&S, x, C, ns, sidx, sw, out, w8 + W.shared, ws_bytes_s, stream);
+  if (s != MOE_OK) return s;
   return launch_gemv(g, st);
 }
 

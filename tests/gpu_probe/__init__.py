@@ -1,4 +1,5 @@
-"""Build and load the matrix-core rounding probes (test infrastructure)."""
+"""Build and load the matrix-core and conversion rounding probes (test
+infrastructure)."""
 import ctypes
 import os
 import subprocess
@@ -24,5 +25,6 @@ def lib():
     P = ctypes.c_void_p
     L.probe_mfma_f32.argtypes = [P, P, P, P, ctypes.c_int, P]
     L.probe_mfma_fp4.argtypes = [P, P, P, P, P, P, ctypes.c_int, P]
-    L.probe_mfma_f32.restype = L.probe_mfma_fp4.restype = ctypes.c_int
+    L.probe_cvt_fp4_bf16.argtypes = [P, P, P, ctypes.c_int, P]
+    L.probe_mfma_f32.restype = L.probe_mfma_fp4.restype = L.probe_cvt_fp4_bf16.restype = ctypes.c_int
     return L

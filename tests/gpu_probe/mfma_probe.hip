@@ -8,6 +8,9 @@
 //   probe_mfma_fp4: v_mfma_scale_f32_16x16x128_f8f6f4 with an e2m1 A and an
 //     e4m3 B, per call a[64][16] and b[64][32] bytes, one scale byte per lane
 //     for each, c[64][4] -> d[64][4].
+//   probe_cvt_fp4_bf16: v_cvt_scalef32_pk_bf16_fp4, per element a dword of 8
+//     e2m1 codes and an fp32 scale -> 8 bf16 (element i reads words[i] and
+//     scales[i], writes out[8i..8i+7]; threads past n do nothing).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -32,7 +35,31 @@ __global__ __launch_bounds__(64) void k_probe_fp4(const uint32_t* a, const uint3
   for (int j = 0; j < 4; ++j) d[4 * i + j] = acc[j];
 }
 
+typedef __bf16 v2bf_t __attribute__((ext_vector_type(2)));
+
+__global__ __launch_bounds__(256) void k_probe_cvt(const uint32_t* words, const float* scales, uint16_t* out,
+                                                   int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const uint32_t w = words[i];
+  const float s = scales[i];
+  v2bf_t v[4];
+  v[0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 0);
+  v[1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 1);
+  v[2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 2);
+  v[3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 3);
+  // each result register holds two bf16 (element 2j in bits 15..0): stored whole
+  uint32_t* o = reinterpret_cast<uint32_t*>(out + 8 * (size_t)i);
+  for (int j = 0; j < 4; ++j) o[j] = __builtin_bit_cast(uint32_t, v[j]);
+}
+
 extern "C" {
+int probe_cvt_fp4_bf16(const uint32_t* words, const float* scales, uint16_t* out, int n, void* stream) {
+  if (n < 1 || !words || !scales || !out) return -1;
+  hipLaunchKernelGGL(k_probe_cvt, dim3((n + 255) / 256), dim3(256), 0, (hipStream_t)stream, words, scales, out, n);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
 int probe_mfma_f32(const float* a, const float* b, const float* c, float* d, int ncalls, void* stream) {
   if (ncalls < 1 || !a || !b || !c || !d) return -1;
   hipLaunchKernelGGL(k_probe_f32, dim3(ncalls), dim3(64), 0, (hipStream_t)stream, a, b, c, d);
