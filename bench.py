@@ -68,6 +68,10 @@ def parse():
     p.add_argument("--calibrate-read", action="store_true",
                    help="only measure the achievable HBM read rate (a plain streaming read "
                         "over 16 GiB, and single launches of one K3 layer's bytes) and print it")
+    p.add_argument("--read-windows", default="",
+                   help="with --calibrate-read: comma-separated window sizes in MB; one line "
+                        "per window with the single-launch rate and time of a plain read of "
+                        "that many bytes")
     return p.parse_args()
 
 
@@ -404,6 +408,17 @@ def main():
         if not os.path.exists(sd.LIB):
             sd.build()
         torch.cuda.set_device(0)
+        if args.read_windows:
+            for mb in (float(v) for v in args.read_windows.split(",")):
+                nbytes = int(mb * 1e6)
+                streaming, single = read_bandwidth(nbytes, passes=2)
+                print(json.dumps({"calibration": "HBM read rate, plain streaming read (16-byte "
+                                                 "non-temporal loads)",
+                                  "window_mb": mb, "single_launch_gbps": round(single, 1),
+                                  "single_launch_us": round(nbytes / (single * 1e3), 2),
+                                  "streaming_16GiB_gbps": round(streaming, 1),
+                                  "peak_gbps": HBM_PEAK_GBPS}), flush=True)
+            return
         streaming, single = read_bandwidth()
         print(json.dumps({"calibration": "HBM read rate, plain streaming read (16-byte "
                                          "non-temporal loads)",

@@ -262,7 +262,7 @@ struct SArgs {
 
 constexpr int kSRowsGU = 4;      // intermediate rows (gate and up) per workgroup
 constexpr int kSRowsDN = 8;      // output rows per workgroup
-constexpr int kSMaxCh = 2;       // 32-element chunks per thread (K <= 16384)
+constexpr int kSMaxCh = 2;       // 32-element chunks per thread at most (K <= 16384)
 
 // sum over one 32-element chunk of w * x: MXFP4 with the power-of-two scale
 // applied in the conversion, NVFP4 as two 16-element block sums times their
@@ -300,7 +300,7 @@ __device__ __forceinline__ uint32_t sscale(const uint8_t* srow, int c) {
 // split K into 32-element chunks (x in registers), every weight load is
 // issued first, sums are reduced over the wave (DPP) and the four waves in
 // order; h = silu(g) * u.
-template <int FMT>
+template <int FMT, int MAXCH>
 __device__ __forceinline__ void sgu_block(const SArgs& a, int j, int i0) {
   constexpr int B = FMT == MOE_FMT_MXFP4 ? 32 : 16;
   __shared__ float s_part[4][2 * kSRowsGU];
@@ -309,10 +309,10 @@ __device__ __forceinline__ void sgu_block(const SArgs& a, int j, int i0) {
   const uint8_t* rec = a.base + (size_t)j * a.stride;
   const uint8_t* cb[2] = {rec + a.off[MOE_T_GATE_CODES], rec + a.off[MOE_T_UP_CODES]};
   const uint8_t* sbp[2] = {rec + a.off[MOE_T_GATE_SCALES], rec + a.off[MOE_T_UP_SCALES]};
-  uint4 q[kSMaxCh][kSRowsGU][2];
-  uint32_t sc[kSMaxCh][kSRowsGU][2];
+  uint4 q[MAXCH][kSRowsGU][2];
+  uint32_t sc[MAXCH][kSRowsGU][2];
 #pragma unroll
-  for (int u = 0; u < kSMaxCh; ++u) {
+  for (int u = 0; u < MAXCH; ++u) {
     const int c = tid + 256 * u;
 #pragma unroll
     for (int r = 0; r < kSRowsGU; ++r)
@@ -332,7 +332,7 @@ __device__ __forceinline__ void sgu_block(const SArgs& a, int j, int i0) {
 #pragma unroll
   for (int r = 0; r < kSRowsGU; ++r) { acc[r][0] = 0.0f; acc[r][1] = 0.0f; }
 #pragma unroll
-  for (int u = 0; u < kSMaxCh; ++u) {
+  for (int u = 0; u < MAXCH; ++u) {
     const int c = tid + 256 * u;
     if (c < nch) {
       float xv[32];
@@ -372,18 +372,18 @@ __device__ __forceinline__ void sgu_block(const SArgs& a, int j, int i0) {
 // Shared-expert down rows n0 .. n0+RD-1: the threads split the concatenated
 // K (every shared expert's I) into 32-element chunks; sdn_load issues the
 // weight loads, sdn_dot the per-thread partial sums.
-template <int RD>
+template <int RD, int MAXCH>
 struct SdnW {
-  uint4 q[kSMaxCh][RD];
-  uint32_t sc[kSMaxCh][RD];
+  uint4 q[MAXCH][RD];
+  uint32_t sc[MAXCH][RD];
 };
 
-template <int FMT, int RD>
-__device__ __forceinline__ void sdn_load(const SArgs& a, int n0, SdnW<RD>& w) {
+template <int FMT, int RD, int MAXCH>
+__device__ __forceinline__ void sdn_load(const SArgs& a, int n0, SdnW<RD, MAXCH>& w) {
   constexpr int B = FMT == MOE_FMT_MXFP4 ? 32 : 16;
   const int tid = threadIdx.x, I = a.I, nchI = I / 32, ntot = a.ns * nchI;
 #pragma unroll
-  for (int u = 0; u < kSMaxCh; ++u) {
+  for (int u = 0; u < MAXCH; ++u) {
     const int cc = tid + 256 * u;
     const int j = cc < ntot ? cc / nchI : 0, c = cc < ntot ? cc - j * nchI : 0;
     const uint8_t* rec = a.base + (size_t)j * a.stride;
@@ -401,13 +401,13 @@ __device__ __forceinline__ void sdn_load(const SArgs& a, int n0, SdnW<RD>& w) {
   }
 }
 
-template <int FMT, int RD>
-__device__ __forceinline__ void sdn_dot(const SArgs& a, const SdnW<RD>& w, float (&acc)[RD]) {
+template <int FMT, int RD, int MAXCH>
+__device__ __forceinline__ void sdn_dot(const SArgs& a, const SdnW<RD, MAXCH>& w, float (&acc)[RD]) {
   const int tid = threadIdx.x, I = a.I, nchI = I / 32, ntot = a.ns * nchI;
 #pragma unroll
   for (int r = 0; r < RD; ++r) acc[r] = 0.0f;
 #pragma unroll
-  for (int u = 0; u < kSMaxCh; ++u) {
+  for (int u = 0; u < MAXCH; ++u) {
     const int cc = tid + 256 * u;
     if (cc < ntot) {
       const int j = cc / nchI, c = cc - j * nchI;
@@ -435,14 +435,14 @@ __device__ __forceinline__ void sdn_dot(const SArgs& a, const SdnW<RD>& w, float
 // expert each).  Both read only x, so one launch streams both weight sets.
 constexpr int kLatRowsA = 8;
 
-template <int FMT>
+template <int FMT, int MAXCH>
 __global__ __launch_bounds__(256) void k_lat_in(GemvArgs g, SArgs s, int nA) {
   const int b = blockIdx.x;
   if (b < nA) {
     gemv_block<kLatRowsA, 1, 4>(g, b);
   } else {
     const int per = s.I / kSRowsGU, q = b - nA;
-    sgu_block<FMT>(s, q / per, (q - (q / per) * per) * kSRowsGU);
+    sgu_block<FMT, MAXCH>(s, q / per, (q - (q / per) * per) * kSRowsGU);
   }
 }
 
@@ -451,18 +451,18 @@ __global__ __launch_bounds__(256) void k_lat_in(GemvArgs g, SArgs s, int nA) {
 // experts' down weights are loaded first, then the W_up rows stream while
 // those loads are in flight.  The sum is formed in the same order as the
 // shared-down launch followed by the accumulating W_up launch.
-template <int FMT>
+template <int FMT, int MAXCH>
 __global__ __launch_bounds__(256) void k_lat_out(GemvArgs g, SArgs s) {
   constexpr int RB = kSRowsDN;
   __shared__ float s_part[4][2 * RB + 1];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n0 = blockIdx.x * RB;
-  SdnW<RB> w;
-  sdn_load<FMT, RB>(s, n0, w);
+  SdnW<RB, MAXCH> w;
+  sdn_load<FMT, RB, MAXCH>(s, n0, w);
   float acc[RB][1], ss[1];
   gemv_dot<RB, 1, 2>(g, n0, acc, ss);
   float sacc[RB];
-  sdn_dot<FMT, RB>(s, w, sacc);
+  sdn_dot<FMT, RB, MAXCH>(s, w, sacc);
 #pragma unroll
   for (int r = 0; r < RB; ++r) {
     const float v = wave_sum_dpp(acc[r][0]);
@@ -502,23 +502,32 @@ SArgs shared_args(const moe_bank* S, const float* x, float* h) {
 }
 
 // One token: routed_down (g) and the shared experts' gate/up into h.
+// The instances hold the chunks per thread that K needs (one up to K = 8192).
 moe_status launch_lat_in(const GemvArgs& g, const SArgs& s, int fmt, hipStream_t st) {
   const int nA = (g.N + kLatRowsA - 1) / kLatRowsA;
   const dim3 grid(nA + s.ns * (s.I / kSRowsGU));
-  if (fmt == MOE_FMT_MXFP4)
-    hipLaunchKernelGGL(k_lat_in<MOE_FMT_MXFP4>, grid, dim3(256), 0, st, g, s, nA);
-  else
-    hipLaunchKernelGGL(k_lat_in<MOE_FMT_NVFP4>, grid, dim3(256), 0, st, g, s, nA);
+  const bool one = s.H / 32 <= 256;
+  if (fmt == MOE_FMT_MXFP4) {
+    if (one) hipLaunchKernelGGL((k_lat_in<MOE_FMT_MXFP4, 1>), grid, dim3(256), 0, st, g, s, nA);
+    else hipLaunchKernelGGL((k_lat_in<MOE_FMT_MXFP4, 2>), grid, dim3(256), 0, st, g, s, nA);
+  } else {
+    if (one) hipLaunchKernelGGL((k_lat_in<MOE_FMT_NVFP4, 1>), grid, dim3(256), 0, st, g, s, nA);
+    else hipLaunchKernelGGL((k_lat_in<MOE_FMT_NVFP4, 2>), grid, dim3(256), 0, st, g, s, nA);
+  }
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_DEVICE;
 }
 
 // One token: out = shared experts' down sum + routed_up (g, with the norm).
 moe_status launch_lat_out(const GemvArgs& g, const SArgs& s, int fmt, hipStream_t st) {
   const dim3 grid(g.N / kSRowsDN);
-  if (fmt == MOE_FMT_MXFP4)
-    hipLaunchKernelGGL(k_lat_out<MOE_FMT_MXFP4>, grid, dim3(256), 0, st, g, s);
-  else
-    hipLaunchKernelGGL(k_lat_out<MOE_FMT_NVFP4>, grid, dim3(256), 0, st, g, s);
+  const bool one = s.ns * (s.I / 32) <= 256;
+  if (fmt == MOE_FMT_MXFP4) {
+    if (one) hipLaunchKernelGGL((k_lat_out<MOE_FMT_MXFP4, 1>), grid, dim3(256), 0, st, g, s);
+    else hipLaunchKernelGGL((k_lat_out<MOE_FMT_MXFP4, 2>), grid, dim3(256), 0, st, g, s);
+  } else {
+    if (one) hipLaunchKernelGGL((k_lat_out<MOE_FMT_NVFP4, 1>), grid, dim3(256), 0, st, g, s);
+    else hipLaunchKernelGGL((k_lat_out<MOE_FMT_NVFP4, 2>), grid, dim3(256), 0, st, g, s);
+  }
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_DEVICE;
 }
 
