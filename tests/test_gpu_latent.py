@@ -120,3 +120,30 @@ def test_latent_k3_shape_token0(C):
                               routed_cache=_K3_WEIGHTS["routed"], shared_cache=_K3_WEIGHTS["shared"])
     assert _rms(ref["routed"]) > 0.1 * _rms(ref["shared"])
     assert_close(out[:1], ref["out"], f"latent K3 C={C} token 0")
+    if C == 1:
+        # gamma = 0 leaves the shared experts alone (the one-token kernels
+        # that fold them into the dense launches)
+        _, _, _, _, _, shared, _ = _run(wl, C, gamma_zero=True)
+        assert_close(shared[:1], ref["shared"], "latent K3 C=1 shared part")
+
+
+def test_latent_k3_one_token_repeat_bit_identical():
+    """The one-token K3 latent layer gives bit-identical outputs on 12
+    back-to-back calls over one workspace, and no bounded wait of the
+    single-launch expert kernel expires."""
+    R = rf()
+    wl = synth.LATENT_WORKLOADS["k3_latent"]
+    say("[latent] K3 shape C=1, 12 back-to-back calls")
+    Wr, x, Wd, Wu, g = synth.latent_inputs(wl, 0, C=1)
+    layer = R.LatentLayer(to_dev(Wr), _bits(Wd), to_dev(g), wl.eps, _bits(Wu),
+                          cached_bank(wl.routed_bank()), cached_bank(wl.shared_bank()))
+    ws = R.LatentWorkspace(layer, wl.k, 1)
+    xd = to_dev(x)
+    outs = [torch.empty((1, wl.H), dtype=torch.float32, device="cuda") for _ in range(12)]
+    for o in outs:
+        R.moe_latent_layer_fwd(layer, xd, 1, wl.k, o, None, None, ws)
+    torch.cuda.synchronize()
+    assert int(ws.tensor[4].item()) == 0
+    first = outs[0].cpu().numpy().view(np.uint32)
+    for i, o in enumerate(outs[1:], 1):
+        assert np.array_equal(o.cpu().numpy().view(np.uint32), first), f"call {i} differs"
