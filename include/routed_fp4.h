@@ -253,7 +253,9 @@ moe_status moe_expert_fwd_mx_mma(const moe_bank *bank, const float *x, int32_t C
  *  - The first call on a device zero-fills the array (a fill kernel on
  *    `stream`); every call on that GPU shares it and leaves it ready for the
  *    next, so calls that overlap on one GPU (other streams, other threads)
- *    race and must be serialised by the caller.
+ *    race and must be serialised by the caller.  Make that first call
+ *    outside any stream capture: a captured zero-fill would be replayed and
+ *    reset the call counter the decode kernel's hand-offs are tagged with.
  *  - error_out: NULL, or a device int32 that receives the decode kernel's
  *    error word (1 if one of its bounded waits expired during this or an
  *    earlier call, whose outputs are then undefined; see above), which is
