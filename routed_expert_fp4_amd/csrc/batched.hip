@@ -581,6 +581,65 @@ __global__ __launch_bounds__(256) void k_brouter(const float* x, const float* Wr
 // order.  A router selection names distinct experts per token, so the pairs
 // of expert e are marked by a token bitmask and a pair's place in the list is
 // the number of earlier tokens in the mask.
+// The same exact top-k as wave_select (same keys, same result), with fewer
+// steps for the usual case, as the single-launch decode kernel selects: T is
+// the largest 16-bit key prefix that at least k lane maxima reach (a 16-step
+// ballot search), so every key of the top k is at or above it; the keys at or
+// above T are gathered into LDS by a per-lane bit mask and a prefix count and
+// each is ranked by the candidates ahead of it (broadcast LDS reads).  More
+// than 64 candidates fall back to wave_select.
+template <int NPL>
+__device__ void wave_select_fast(uint64_t (&ck)[NPL], const float (&lv)[NPL], int k, SelectLds& S) {
+  const int lane = threadIdx.x & 63;
+  uint32_t m = 0;                                  // this lane's largest 32-bit key
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) {
+    const uint32_t kk = (uint32_t)(ck[i] >> 32);
+    m = kk > m ? kk : m;
+  }
+  uint32_t T = 0;
+  for (int bit = 31; bit >= 16; --bit) {
+    const uint32_t c = T | (1u << bit);
+    if (__popcll(__ballot(m >= c)) >= k) T = c;
+  }
+  uint32_t cm = 0;
+#pragma unroll
+  for (int i = 0; i < NPL; ++i)
+    cm |= (ck[i] != 0 && (uint32_t)(ck[i] >> 32) >= T) ? (1u << i) : 0u;
+  const int cnt = __popc(cm);
+  const int incl = wave_incl_scan(cnt);
+  const int n = __builtin_amdgcn_readlane(incl, 63);
+  if (n > 64) {
+    wave_select<NPL>(ck, lv, k, S);
+    return;
+  }
+  int pos = incl - cnt;
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) {
+    if ((cm >> i) & 1u) {
+      S.cand_key[pos] = ck[i];
+      S.cand_l[pos] = lv[i];
+      ++pos;
+    }
+  }
+  // zero keys after the last candidate up to a multiple of 4 (never ahead of a real key)
+  if (lane >= n && lane < ((n + 3) & ~3)) S.cand_key[lane] = 0;
+  wave_lds_fence();
+  const uint64_t mine = lane < n ? S.cand_key[lane] : 0;
+  const float ml = lane < n ? S.cand_l[lane] : 0.0f;
+  int rk = 0;                                      // candidates ahead of this one
+  for (int j = 0; j < n; j += 4) {
+    const uint64_t c0 = S.cand_key[j], c1 = S.cand_key[j + 1];
+    const uint64_t c2 = S.cand_key[j + 2], c3 = S.cand_key[j + 3];
+    rk += (c0 > mine) + (c1 > mine) + (c2 > mine) + (c3 > mine);
+  }
+  if (lane < n && rk < k) {
+    S.sel_e[rk] = (int32_t)~(uint32_t)mine;
+    S.sel_l[rk] = ml;
+  }
+  wave_lds_fence();
+}
+
 template <int NW>
 __global__ __launch_bounds__(64 * NW) void k_btopk(const float* logits, const float* lpart, int ksplit,
                                                    float* logits_out, int C, int E, int k,
@@ -623,7 +682,7 @@ __global__ __launch_bounds__(64 * NW) void k_btopk(const float* logits, const fl
       if (lpart && logits_out && e < E) logits_out[(size_t)t * E + e] = lv[i];
       ck[i] = e < E ? sel_key(lv[i], e) : 0;
     }
-    wave_select<NPL>(ck, lv, k, S[wave]);
+    wave_select_fast<NPL>(ck, lv, k, S[wave]);
     const float l = lane < k ? S[wave].sel_l[lane] : 0.0f;
     const float wt = route_weight(l, lane, k);
     if (lane < k) {
