@@ -26,5 +26,7 @@ def lib():
     L.probe_mfma_f32.argtypes = [P, P, P, P, ctypes.c_int, P]
     L.probe_mfma_fp4.argtypes = [P, P, P, P, P, P, ctypes.c_int, P]
     L.probe_cvt_fp4_bf16.argtypes = [P, P, P, ctypes.c_int, P]
-    L.probe_mfma_f32.restype = L.probe_mfma_fp4.restype = L.probe_cvt_fp4_bf16.restype = ctypes.c_int
+    L.probe_mfma_4x4_bf16.argtypes = [P, P, P, P, ctypes.c_int, P]
+    for f in (L.probe_mfma_f32, L.probe_mfma_fp4, L.probe_cvt_fp4_bf16, L.probe_mfma_4x4_bf16):
+        f.restype = ctypes.c_int
     return L

@@ -11,6 +11,9 @@
 //   probe_cvt_fp4_bf16: v_cvt_scalef32_pk_bf16_fp4, per element a dword of 8
 //     e2m1 codes and an fp32 scale -> 8 bf16 (element i reads words[i] and
 //     scales[i], writes out[8i..8i+7]; threads past n do nothing).
+//   probe_mfma_4x4_bf16: v_mfma_f32_4x4x4_16b_bf16, per call and lane 4 bf16
+//     of A, 4 bf16 of B and 4 fp32 of the accumulator -> 4 fp32 (lane l of
+//     call c reads and writes element c * 64 + l of each array).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -53,7 +56,22 @@ __global__ __launch_bounds__(256) void k_probe_cvt(const uint32_t* words, const 
   for (int j = 0; j < 4; ++j) o[j] = __builtin_bit_cast(uint32_t, v[j]);
 }
 
+typedef short v4s_t __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(64) void k_probe_m4(const v4s_t* a, const v4s_t* b, const v4f_t* c, v4f_t* d) {
+  const size_t i = (size_t)blockIdx.x * 64 + threadIdx.x;
+  d[i] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(a[i], b[i], c[i], 0, 0, 0);
+}
+
 extern "C" {
+int probe_mfma_4x4_bf16(const void* a, const void* b, const float* c, float* d, int ncalls, void* stream) {
+  if (ncalls < 1 || !a || !b || !c || !d) return -1;
+  hipLaunchKernelGGL(k_probe_m4, dim3(ncalls), dim3(64), 0, (hipStream_t)stream,
+                     reinterpret_cast<const v4s_t*>(a), reinterpret_cast<const v4s_t*>(b),
+                     reinterpret_cast<const v4f_t*>(c), reinterpret_cast<v4f_t*>(d));
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
 int probe_cvt_fp4_bf16(const uint32_t* words, const float* scales, uint16_t* out, int n, void* stream) {
   if (n < 1 || !words || !scales || !out) return -1;
   hipLaunchKernelGGL(k_probe_cvt, dim3((n + 255) / 256), dim3(256), 0, (hipStream_t)stream, words, scales, out, n);
