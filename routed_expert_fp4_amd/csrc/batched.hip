@@ -971,8 +971,8 @@ moe_status launch_bdma(const BArgs& a, dim3 grid, hipStream_t st) {
 // Work split.  The row steps of all distinct experts (GU: 32 rows of I, one
 // gate and up row per lane group; DN: 64 rows of H, two per lane group) are
 // laid end to end and cut into one contiguous range per workgroup of equal
-// cost, a row step of expert u costing passes_u * kDCostW + tokens_u (weight
-// bytes plus per-token arithmetic).  A workgroup walks its range expert by
+// cost, a row step of expert u costing passes_u * dm_costw(K) + 4 tokens_u
+// (weight bytes plus per-token work, in quarters of one token's work).  A workgroup walks its range expert by
 // expert; for each it stages the activations of up to ntp pairs in LDS
 // (fp32, 36 floats per 32 so the 16 lanes of a group hit distinct banks) and
 // streams its rows through a register pipeline of kDPipe stages of kDSC
@@ -981,7 +981,10 @@ constexpr int kDWG = 512;                  // threads per workgroup
 constexpr int kDGrp = kDWG / 16;           // 16-lane groups per workgroup
 constexpr int kDSC = 2;                    // 16-byte chunks per lane per pipeline stage
 constexpr int kDPipe = 3;                  // register buffers of the weight stream
-constexpr int kDCostW = 1;                 // cost of one weight pass of a row step, in tokens
+// One weight pass of a row step in quarters of a token's work on it (the
+// matrix-core products, their LDS operands and the epilogue): per-workgroup
+// clocks put a pass of a row step (64 rows of K) at about K / 580 tokens.
+__device__ __forceinline__ int dm_costw(int K) { return (4 * K + 290) / 580; }
 constexpr int kDLds = 131072;              // LDS bytes for staged activations
 constexpr int kDMaxU = MOE_MAX_DECODE_TOKENS * MOE_MAX_TOPK;   // distinct experts at most
 
@@ -998,84 +1001,112 @@ struct DArgs {
   int ntp;                // pairs staged per pass (1, 2, 4 or 8)
 };
 
-// acc[r][t] += sum over one 32-element chunk of w_r * x_t for NR rows and the
-// first nt (<= NT) staged pairs, one 8-element dword at a time.  MXFP4: the
-// conversion applies the power-of-two scale exactly, so every product goes
-// straight into acc.  NVFP4: e2m1 values are summed per 16-element block and
-// the block's e4m3 scale multiplies the block sum.
-template <int FMT, int NR, int NT>
-__device__ __forceinline__ void chunk_dot(const uint4 (&q)[NR], const uint32_t (&sc)[NR],
-                                          const float* xs, int xoff, int ts, int nt,
-                                          float (&acc)[NR][NT]) {
+// Staged activations of the matrix-core streams: two bf16 planes (hi, lo) of
+// every staged pair, pair t of plane p at byte p * dm_ps + t * dm_ts.  The
+// strides are 32 and 16 bytes past a multiple of 128, so the 8 lanes of each
+// phase of a 16-byte LDS read (4 columns x 2 chunks) hit distinct banks.
+__host__ __device__ __forceinline__ int dm_ts(int K) { return 2 * K + 32; }
+__host__ __device__ __forceinline__ int dm_slots(int ntp) { return ntp < 2 ? 2 : ntp; }
+__host__ __device__ __forceinline__ int dm_ps(int K, int ntp) {
+  return (dm_slots(ntp) * dm_ts(K) + 127) / 128 * 128 + 16;
+}
+
+typedef short bf16x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ bf16x4_t as_bf16x4(uint32_t lo, uint32_t hi) {
+  return __builtin_bit_cast(bf16x4_t, u32x2_t{lo, hi});
+}
+
+// acc[r][g] += one 32-element chunk of NR rows against the pairs of column
+// group g (< ng), on the 4 x 4 x 4 matrix-core product of 16 blocks: lane
+// 4b + i holds row i's chunk b (A: 4 K values per product, 8 products per
+// chunk), lane 4b + j holds column j of the same K values (B: plane j & 1 of
+// pair 2g + (j >> 1)), and lane 4b + j's accumulator i is row i, column j,
+// summed over chunk b's K values only (the epilogue adds the 16 blocks).
+// MXFP4: the conversion applies the block's power-of-two scale exactly.
+// NVFP4: each 16-element half is summed on its own and multiplied by its
+// row's e4m3 scale, which the lane takes from the quad lane that loaded it.
+template <int FMT, int NR, int G>
+__device__ __forceinline__ void chunk_mfma(const uint4 (&q)[NR], const uint32_t (&sc)[NR],
+                                           const uint8_t* xb, uint32_t gstride, int nt,
+                                           f32x4_t (&acc)[NR][G]) {
+  const int ng = (nt + 1) / 2;
   constexpr bool MX = FMT == MOE_FMT_MXFP4;
-  float blk[NR][NT];
-  float ms[NR];
-  if (MX) {
+  bf16x4_t av[NR][8];
 #pragma unroll
-    for (int r = 0; r < NR; ++r) ms[r] = __uint_as_float((sc[r] & 0xFFu) << 23);   // 2^(sc-127)
-  }
+  for (int r = 0; r < NR; ++r) {
+    const float s = MX ? __uint_as_float((sc[r] & 0xFFu) << 23) : 1.0f;
 #pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    if (!MX && (d & 1) == 0) {
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        if (t >= nt) break;
-#pragma unroll
-        for (int r = 0; r < NR; ++r) blk[r][t] = 0.0f;
-      }
+    for (int d = 0; d < 4; ++d) {
+      const uint32_t wd = (d == 0) ? q[r].x : (d == 1) ? q[r].y : (d == 2) ? q[r].z : q[r].w;
+      const uint32_t p0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, s, 0));
+      const uint32_t p1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, s, 1));
+      const uint32_t p2 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, s, 2));
+      const uint32_t p3 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, s, 3));
+      av[r][2 * d] = as_bf16x4(p0, p1);
+      av[r][2 * d + 1] = as_bf16x4(p2, p3);
     }
-    float wv[NR][8];
+  }
+  float ns[NR][2][4];                    // NVFP4: [row stream][half][row i of the quad]
+  if (!MX) {
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
-      const uint32_t wd = (d == 0) ? q[r].x : (d == 1) ? q[r].y : (d == 2) ? q[r].z : q[r].w;
-      const float s = MX ? ms[r] : 1.0f;
-      const auto v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd, s, 0);
-      const auto v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd, s, 1);
-      const auto v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd, s, 2);
-      const auto v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd, s, 3);
-      wv[r][0] = v0[0]; wv[r][1] = v0[1]; wv[r][2] = v1[0]; wv[r][3] = v1[1];
-      wv[r][4] = v2[0]; wv[r][5] = v2[1]; wv[r][6] = v3[0]; wv[r][7] = v3[1];
+      const int w0 = __builtin_amdgcn_mov_dpp((int)sc[r], 0x00, 0xF, 0xF, false);
+      const int w1 = __builtin_amdgcn_mov_dpp((int)sc[r], 0x55, 0xF, 0xF, false);
+      const int w2 = __builtin_amdgcn_mov_dpp((int)sc[r], 0xAA, 0xF, 0xF, false);
+      const int w3 = __builtin_amdgcn_mov_dpp((int)sc[r], 0xFF, 0xF, 0xF, false);
+      ns[r][0][0] = __builtin_amdgcn_cvt_f32_fp8(w0, 0); ns[r][1][0] = __builtin_amdgcn_cvt_f32_fp8(w0, 1);
+      ns[r][0][1] = __builtin_amdgcn_cvt_f32_fp8(w1, 0); ns[r][1][1] = __builtin_amdgcn_cvt_f32_fp8(w1, 1);
+      ns[r][0][2] = __builtin_amdgcn_cvt_f32_fp8(w2, 0); ns[r][1][2] = __builtin_amdgcn_cvt_f32_fp8(w2, 1);
+      ns[r][0][3] = __builtin_amdgcn_cvt_f32_fp8(w3, 0); ns[r][1][3] = __builtin_amdgcn_cvt_f32_fp8(w3, 1);
     }
+  }
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      if (t >= nt) break;
-      const float4* x4 = reinterpret_cast<const float4*>(xs + t * ts + xoff);
-      const float4 xa = x4[2 * d], xb = x4[2 * d + 1];
-#pragma unroll
-      for (int r = 0; r < NR; ++r) {
-        float b = MX ? acc[r][t] : blk[r][t];
-        b += wv[r][0] * xa.x; b += wv[r][1] * xa.y; b += wv[r][2] * xa.z; b += wv[r][3] * xa.w;
-        b += wv[r][4] * xb.x; b += wv[r][5] * xb.y; b += wv[r][6] * xb.z; b += wv[r][7] * xb.w;
-        if (MX) acc[r][t] = b;
-        else blk[r][t] = b;
-      }
+  for (int g = 0; g < G; ++g) {
+    if (g >= ng) break;
+    // a column of a pair past the pass's count stays zero without an LDS read
+    uint4 b0 = make_uint4(0u, 0u, 0u, 0u), b1 = b0, b2 = b0, b3 = b0;
+    if (2 * g + ((threadIdx.x >> 1) & 1) < nt) {
+      const uint4* bp = reinterpret_cast<const uint4*>(xb + g * gstride);
+      b0 = bp[0]; b1 = bp[1]; b2 = bp[2]; b3 = bp[3];
     }
-    if (!MX && (d & 1)) {
+    const bf16x4_t bv[8] = {as_bf16x4(b0.x, b0.y), as_bf16x4(b0.z, b0.w), as_bf16x4(b1.x, b1.y),
+                            as_bf16x4(b1.z, b1.w), as_bf16x4(b2.x, b2.y), as_bf16x4(b2.z, b2.w),
+                            as_bf16x4(b3.x, b3.y), as_bf16x4(b3.z, b3.w)};
 #pragma unroll
-      for (int r = 0; r < NR; ++r) {
-        const float s = e4m3_to_f32((sc[r] >> (8 * (d >> 1))) & 0xFFu);
+    for (int r = 0; r < NR; ++r) {
+      if (MX) {
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          if (t >= nt) break;
-          acc[r][t] += s * blk[r][t];
+        for (int m = 0; m < 8; ++m)
+          acc[r][g] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(av[r][m], bv[m], acc[r][g], 0, 0, 0);
+      } else {
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          f32x4_t t = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+          for (int m = 4 * hf; m < 4 * hf + 4; ++m)
+            t = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(av[r][m], bv[m], t, 0, 0, 0);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[r][g][i] += ns[r][hf][i] * t[i];
         }
       }
     }
-    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-// One lane group's stream over `rows` rows of one expert (row ri at byte
-// offset coff[r] + ri * rstride of stream r; scales likewise), kch chunks of
-// 256 bytes per row, pipelined across rows.  done(ri, acc) gets the lane's
-// partial sums after each row's last chunk.
-template <int FMT, int NR, int NT, class Done>
-__device__ __forceinline__ void dstream_rows(const __amdgpu_buffer_rsrc_t (&crs)[NR],
-                                             const __amdgpu_buffer_rsrc_t (&srs)[NR],
-                                             const uint32_t (&coff)[NR], const uint32_t (&soff)[NR],
-                                             uint32_t rstride, uint32_t sstride, int rows, int kch,
-                                             const float* xs, int ts, int nt, Done done) {
-  const int l16 = threadIdx.x & 15;
+// One wave's stream over `rows` row groups of one expert (4 rows each; lane
+// 4b + i loads row i's 16-byte slot b of each 256-byte chunk; row group ri at
+// byte offset coff[r] + ri * rstride of stream r, scales likewise), kch
+// chunks per row, pipelined across row groups.  xb: this lane's B column in
+// LDS (plane, pair and slot applied), chunks 1024 bytes apart.  done(ri, acc)
+// gets the accumulators after each row group's last chunk.
+template <int FMT, int NR, int G, class Done>
+__device__ __forceinline__ void dmma_rows(const __amdgpu_buffer_rsrc_t (&crs)[NR],
+                                          const __amdgpu_buffer_rsrc_t (&srs)[NR],
+                                          const uint32_t (&coff)[NR], const uint32_t (&soff)[NR],
+                                          uint32_t rstride, uint32_t sstride, int rows, int kch,
+                                          const uint8_t* xb, uint32_t gstride, int nt, Done done) {
   constexpr int SB = (FMT == MOE_FMT_MXFP4) ? 16 : 32;   // scale bytes per chunk of a row
   uint4 q[kDPipe][kDSC][NR];
   uint32_t sc[kDPipe][kDSC][NR];
@@ -1101,22 +1132,22 @@ __device__ __forceinline__ void dstream_rows(const __amdgpu_buffer_rsrc_t (&crs)
       if (++lc == kch) { lc = 0; ++lrow; }
     }
   };
-  float acc[NR][NT];
+  f32x4_t acc[NR][G];
 #pragma unroll
   for (int r = 0; r < NR; ++r)
 #pragma unroll
-    for (int t = 0; t < NT; ++t) acc[r][t] = 0.0f;
-  auto fma = [&](const uint4 (&qq)[kDSC][NR], const uint32_t (&ss)[kDSC][NR]) {
+    for (int g = 0; g < G; ++g) acc[r][g] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  auto step = [&](const uint4 (&qq)[kDSC][NR], const uint32_t (&ss)[kDSC][NR]) {
 #pragma unroll
     for (int b = 0; b < kDSC; ++b) {
       if (crow < rows) {
-        chunk_dot<FMT, NR, NT>(qq[b], ss[b], xs, (l16 + 16 * cc) * 36, ts, nt, acc);
+        chunk_mfma<FMT, NR, G>(qq[b], ss[b], xb + 1024 * cc, gstride, nt, acc);
         if (cc == kch - 1) {
           done(crow, acc);
 #pragma unroll
           for (int r = 0; r < NR; ++r)
 #pragma unroll
-            for (int t = 0; t < NT; ++t) acc[r][t] = 0.0f;
+            for (int g = 0; g < G; ++g) acc[r][g] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
         }
         if (++cc == kch) { cc = 0; ++crow; }
       }
@@ -1132,9 +1163,31 @@ __device__ __forceinline__ void dstream_rows(const __amdgpu_buffer_rsrc_t (&crs)
       __builtin_amdgcn_sched_barrier(0);
       load(q[(j + kDPipe - 1) % kDPipe], sc[(j + kDPipe - 1) % kDPipe]);
       __builtin_amdgcn_sched_barrier(0);
-      fma(q[j], sc[j]);
+      step(q[j], sc[j]);
     }
   }
+}
+
+// Sum of a row-group accumulator over the 16 blocks (lanes 4b + j, same j)
+// and over the hi and lo planes (columns j and j ^ 1).  Returns, in each lane
+// of 16-lane row q, row q's dot product with pair 2g + ((lane >> 1) & 1): the
+// four rows' sums are first split across the lane rows (two exchanges that
+// each halve what a lane carries), then the row's four blocks of the same
+// column and the two planes are added with DPP.  The same lane always holds
+// the result a store takes, so the sums are the same bits on every call.
+__device__ __forceinline__ float dm_reduce(const f32x4_t& v) {
+  const int q = (threadIdx.x >> 4) & 3;
+  const bool up = q >= 2, odd = q & 1;
+  float k0 = up ? v[2] : v[0], k1 = up ? v[3] : v[1];
+  const float s0 = up ? v[0] : v[2], s1 = up ? v[1] : v[3];
+  k0 += __shfl_xor(s0, 32, 64);
+  k1 += __shfl_xor(s1, 32, 64);
+  float k = odd ? k1 : k0;
+  k += __shfl_xor(odd ? k0 : k1, 16, 64);
+  k += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(k), 0x124, 0xF, 0xF, false));  // row_ror:4
+  k += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(k), 0x128, 0xF, 0xF, false));  // row_ror:8
+  k += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(k), 0xB1, 0xF, 0xF, false));   // quad [1,0,3,2]
+  return k;
 }
 
 // Workgroup-wide exclusive scan (blockDim.x = kDWG).
@@ -1157,20 +1210,31 @@ __device__ int block_excl_scan_dwg(int v, int* s_w, int* total) {
 
 // One pass of one distinct expert's rows [rsb, rse) of row steps against NTC
 // staged pairs (nt of them used): the gate/up rows with SwiGLU into h, or the
-// down rows times the routing weight into part.  NTC is a compile-time count
-// so that no activation of an unused pair slot is read: the kernel picks the
-// smallest instance that holds the pass.
+// down rows times the routing weight into part.  NTC is a compile-time bound
+// (2, 4 or 8 pairs: 1, 2 or 4 column groups of the matrix-core product), so
+// that no column group past the pass's pairs is multiplied.  Wave w's rows of
+// a row step are 4w .. 4w + 3 (gate/up: of the step's 32; down: of each half
+// of its 64).
 template <int FMT, bool GU, int NTC>
 __device__ __forceinline__ void dstream_pass(const DArgs& a, const uint8_t* rec, int rsb, int rse,
-                                             const float* xs, int ts, int nt, const int* s_pairs) {
+                                             const uint8_t* xs, int ps, int ts, int nt,
+                                             const int* s_pairs) {
   const int H = a.H, I = a.I, K = GU ? H : I;
   const int B = (FMT == MOE_FMT_MXFP4) ? 32 : 16;
   constexpr int RS = GU ? kDGrp : 2 * kDGrp;          // rows per row step
+  constexpr int G = NTC / 2;                          // column groups of 2 pairs
   const int kch = K / 512;                            // 256-byte chunks per row
-  const int grp = threadIdx.x >> 4, l16 = threadIdx.x & 15;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int il = lane & 3, bq = lane >> 2;            // load: row il of the wave's 4, slot bq
+  const int iw = lane >> 4, tw = (lane >> 1) & 1;       // store: row iw, pair 2g + tw
+  const bool writer = (lane & 13) == 0;                   // lanes 16 iw + 2 tw
   const uint32_t rowb = (uint32_t)(K / 2), srowb = (uint32_t)(K / B);
-  constexpr int NT = NTC;
   const int rows = rse - rsb;
+  const int ng = (nt + 1) / 2;
+  const uint8_t* xb = xs + (lane & 1) * ps + ((lane >> 1) & 1) * ts + 64 * bq;
+  const uint32_t gstride = 2u * (uint32_t)ts;
+  const int grp = 4 * wave + il;                      // this lane's load row within a row step
+  const int gw = 4 * wave + iw;                       // this lane's store row
   if (GU) {
     __amdgpu_buffer_rsrc_t crs[2], srs[2];
     crs[0] = view(rec + a.off[MOE_T_GATE_CODES], (uint32_t)I * rowb);
@@ -1178,23 +1242,24 @@ __device__ __forceinline__ void dstream_pass(const DArgs& a, const uint8_t* rec,
     srs[0] = view(rec + a.off[MOE_T_GATE_SCALES], (uint32_t)I * srowb);
     srs[1] = view(rec + a.off[MOE_T_UP_SCALES], (uint32_t)I * srowb);
     const int row0 = rsb * RS + grp;
-    const uint32_t coff[2] = {(uint32_t)row0 * rowb + l16 * 16, (uint32_t)row0 * rowb + l16 * 16};
-    const uint32_t soff[2] = {(uint32_t)row0 * srowb + l16 * (32 / B), (uint32_t)row0 * srowb + l16 * (32 / B)};
+    const uint32_t coff[2] = {(uint32_t)row0 * rowb + bq * 16, (uint32_t)row0 * rowb + bq * 16};
+    const uint32_t soff[2] = {(uint32_t)row0 * srowb + bq * (32 / B), (uint32_t)row0 * srowb + bq * (32 / B)};
     float gg = 1.0f, gu = 1.0f;
     if (FMT == MOE_FMT_NVFP4) {
       const float* gl = reinterpret_cast<const float*>(rec + a.off[MOE_T_GLOBALS]);
       gg = gl[0];
       gu = gl[1];
     }
-    dstream_rows<FMT, 2, NT>(crs, srs, coff, soff, RS * rowb, RS * srowb, rows, kch, xs, ts, nt,
-                             [&](int ri, float (&acc)[2][NT]) {
-      const int j = row0 + ri * RS;
+    dmma_rows<FMT, 2, G>(crs, srs, coff, soff, RS * rowb, RS * srowb, rows, kch, xb, gstride, nt,
+                         [&](int ri, f32x4_t (&acc)[2][G]) {
+      const int j = (rsb + ri) * RS + gw;
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        if (t >= nt) break;
-        const float gs = group16_sum(acc[0][t]);
-        const float us = group16_sum(acc[1][t]);
-        if (l16 == 0) a.h[(size_t)s_pairs[t] * I + j] = silu(gg * gs) * (gu * us);
+      for (int g = 0; g < G; ++g) {
+        if (g >= ng) break;
+        const float gs = dm_reduce(acc[0][g]);
+        const float us = dm_reduce(acc[1][g]);
+        const int t = 2 * g + tw;
+        if (writer && t < nt) a.h[(size_t)s_pairs[t] * I + j] = silu(gg * gs) * (gu * us);
       }
     });
   } else {
@@ -1202,22 +1267,23 @@ __device__ __forceinline__ void dstream_pass(const DArgs& a, const uint8_t* rec,
     crs[0] = crs[1] = view(rec + a.off[MOE_T_DOWN_CODES], (uint32_t)H * rowb);
     srs[0] = srs[1] = view(rec + a.off[MOE_T_DOWN_SCALES], (uint32_t)H * srowb);
     const int row0 = rsb * RS + grp;                // and row0 + kDGrp
-    const uint32_t coff[2] = {(uint32_t)row0 * rowb + l16 * 16, (uint32_t)(row0 + kDGrp) * rowb + l16 * 16};
-    const uint32_t soff[2] = {(uint32_t)row0 * srowb + l16 * (32 / B),
-                              (uint32_t)(row0 + kDGrp) * srowb + l16 * (32 / B)};
+    const uint32_t coff[2] = {(uint32_t)row0 * rowb + bq * 16, (uint32_t)(row0 + kDGrp) * rowb + bq * 16};
+    const uint32_t soff[2] = {(uint32_t)row0 * srowb + bq * (32 / B),
+                              (uint32_t)(row0 + kDGrp) * srowb + bq * (32 / B)};
     float gd = 1.0f;
     if (FMT == MOE_FMT_NVFP4) gd = reinterpret_cast<const float*>(rec + a.off[MOE_T_GLOBALS])[2];
-    dstream_rows<FMT, 2, NT>(crs, srs, coff, soff, RS * rowb, RS * srowb, rows, kch, xs, ts, nt,
-                             [&](int ri, float (&acc)[2][NT]) {
-      const int j = row0 + ri * RS;
+    dmma_rows<FMT, 2, G>(crs, srs, coff, soff, RS * rowb, RS * srowb, rows, kch, xb, gstride, nt,
+                         [&](int ri, f32x4_t (&acc)[2][G]) {
+      const int j = (rsb + ri) * RS + gw;
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        if (t >= nt) break;
-        const int p = s_pairs[t];
-        const float wp = a.w[p] * gd;
-        const float y0 = group16_sum(acc[0][t]);
-        const float y1 = group16_sum(acc[1][t]);
-        if (l16 == 0) {
+      for (int g = 0; g < G; ++g) {
+        if (g >= ng) break;
+        const float y0 = dm_reduce(acc[0][g]);
+        const float y1 = dm_reduce(acc[1][g]);
+        const int t = 2 * g + tw;
+        if (writer && t < nt) {
+          const int p = s_pairs[t];
+          const float wp = a.w[p] * gd;
           a.part[(size_t)p * H + j] = wp * y0;
           a.part[(size_t)p * H + j + kDGrp] = wp * y1;
         }
@@ -1228,7 +1294,7 @@ __device__ __forceinline__ void dstream_pass(const DArgs& a, const uint8_t* rec,
 
 template <int FMT, bool GU, int NT>
 __global__ __launch_bounds__(kDWG) void k_dstream(DArgs a) {
-  extern __shared__ __attribute__((aligned(16))) float xs[];   // [ntp][K / 32 * 36]
+  extern __shared__ __attribute__((aligned(16))) uint8_t xs[];   // [2][dm_slots(ntp)] bf16 rows
   __shared__ int s_pref[kDMaxU + 1];
   __shared__ int s_w[kDWG / 64];
   __shared__ int s_bound[2];
@@ -1239,12 +1305,12 @@ __global__ __launch_bounds__(kDWG) void k_dstream(DArgs a) {
   const int H = a.H, I = a.I, K = GU ? H : I, N = GU ? I : H;
   constexpr int RS = GU ? kDGrp : 2 * kDGrp;          // rows per row step
   const int nrs = N / RS;
-  const int ts = K / 32 * 36;                         // LDS floats per staged pair
   const int ntp = a.ntp;
+  const int ts = dm_ts(K), ps = dm_ps(K, ntp);        // LDS bytes: pair and plane strides
 
   // cost prefix over the distinct experts, then this workgroup's range
   const int ntok = tid < CK ? a.disp[disp_untok(CK) + tid] : 0;   // loaded beside nu
-  const int wu = tid < nu ? ((ntok + ntp - 1) / ntp) * kDCostW + ntok : 0;
+  const int wu = tid < nu ? ((ntok + ntp - 1) / ntp) * dm_costw(K) + 4 * ntok : 0;
   int total = 0;
   const int pre = block_excl_scan_dwg(tid < nu ? wu * nrs : 0, s_w, &total);
   if (tid < nu) s_pref[tid] = pre;
@@ -1276,19 +1342,31 @@ __global__ __launch_bounds__(kDWG) void k_dstream(DArgs a) {
       __syncthreads();                                  // the previous pass is done with LDS
       if (tid < nt) s_pairs[tid] = a.disp[disp_upair(CK) + u * a.C + p0 + tid];
       __syncthreads();
-      for (int q = tid * 4; q < nt * K; q += kDWG * 4) {
+      // each activation as hi = bf16(v) and lo = bf16(v - hi) (v - hi is exact
+      // in fp32; hi + lo is v to within 2^-18 relative); the pair slot after
+      // an odd count is zero, so the last column group's second pair adds 0
+      const int ntc = (nt + 1) & ~1;
+      for (int q = tid * 4; q < ntc * K; q += kDWG * 4) {
         const int t = q / K, kk = q - t * K;
-        const int p = s_pairs[t];
-        const float4 v = GU ? *reinterpret_cast<const float4*>(a.x + (size_t)(p / a.k) * H + kk)
-                            : *reinterpret_cast<const float4*>(a.h + (size_t)p * I + kk);
-        *reinterpret_cast<float4*>(xs + t * ts + kk + (kk >> 5) * 4) = v;
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (t < nt) {
+          const int p = s_pairs[t];
+          v = GU ? *reinterpret_cast<const float4*>(a.x + (size_t)(p / a.k) * H + kk)
+                 : *reinterpret_cast<const float4*>(a.h + (size_t)p * I + kk);
+        }
+        const uint16_t h0 = bf16_bits(v.x), h1 = bf16_bits(v.y), h2 = bf16_bits(v.z), h3 = bf16_bits(v.w);
+        const uint16_t l0 = bf16_bits(v.x - bf16_float(h0)), l1 = bf16_bits(v.y - bf16_float(h1));
+        const uint16_t l2 = bf16_bits(v.z - bf16_float(h2)), l3 = bf16_bits(v.w - bf16_float(h3));
+        uint8_t* d = xs + t * ts + 2 * kk;
+        *reinterpret_cast<uint2*>(d) = make_uint2(h0 | ((uint32_t)h1 << 16), h2 | ((uint32_t)h3 << 16));
+        *reinterpret_cast<uint2*>(d + ps) = make_uint2(l0 | ((uint32_t)l1 << 16), l2 | ((uint32_t)l3 << 16));
       }
       __syncthreads();
-      // a pass of one pair runs the one-pair instance, so that no unused pair
-      // slot's activations are read; others the workgroup's own
-      if (NT == 1 || nt == 1) dstream_pass<FMT, GU, 1>(a, rec, rsb, rse, xs, ts, 1, s_pairs);
-      else if (NT == 2 || nt == 2) dstream_pass<FMT, GU, 2>(a, rec, rsb, rse, xs, ts, 2, s_pairs);
-      else dstream_pass<FMT, GU, NT>(a, rec, rsb, rse, xs, ts, nt, s_pairs);
+      // the smallest instance that holds the pass, so that no column group
+      // past its pairs is multiplied
+      if (NT <= 2 || nt <= 2) dstream_pass<FMT, GU, 2>(a, rec, rsb, rse, xs, ps, ts, nt, s_pairs);
+      else if (NT == 4 || nt <= 4) dstream_pass<FMT, GU, 4>(a, rec, rsb, rse, xs, ps, ts, nt, s_pairs);
+      else dstream_pass<FMT, GU, 8>(a, rec, rsb, rse, xs, ps, ts, nt, s_pairs);
     }
   }
 }
@@ -1320,12 +1398,11 @@ moe_status launch_dstream(const DArgs& a, int grid, int lds, hipStream_t st) {
   }
 }
 
-// Pairs per activation pass: the largest of 8, 4, 2, 1 whose staged rows
-// (K / 32 * 36 floats each) fit the LDS budget; 0 if not even one does.
+// Pairs per activation pass: the largest of 8, 4, 2, 1 whose two bf16 planes
+// fit the LDS budget; 0 if not even one does.
 int dstream_ntp(int K) {
-  const int per = K / 32 * 36 * (int)sizeof(float);
   for (int n = 8; n >= 1; n >>= 1)
-    if (n * per <= kDLds) return n;
+    if (2 * dm_ps(K, n) <= kDLds) return n;
   return 0;
 }
 
@@ -1453,12 +1530,12 @@ moe_status launch_batched_decode(const moe_bank* b, const float* x, int C, int k
   const int grid = dstream_grid();
   moe_status m;
   a.ntp = ntg;
-  const int lds_g = ntg * (H / 32 * 36) * (int)sizeof(float);
+  const int lds_g = 2 * dm_ps(H, ntg);
   if (b->format == MOE_FMT_MXFP4) m = launch_dstream<MOE_FMT_MXFP4, true>(a, grid, lds_g, st);
   else m = launch_dstream<MOE_FMT_NVFP4, true>(a, grid, lds_g, st);
   if (m != MOE_OK) return m;
   a.ntp = ntd;
-  const int lds_d = ntd * (I / 32 * 36) * (int)sizeof(float);
+  const int lds_d = 2 * dm_ps(I, ntd);
   if (b->format == MOE_FMT_MXFP4) m = launch_dstream<MOE_FMT_MXFP4, false>(a, grid, lds_d, st);
   else m = launch_dstream<MOE_FMT_NVFP4, false>(a, grid, lds_d, st);
   if (m != MOE_OK) return m;
