@@ -971,7 +971,7 @@ moe_status launch_bdma(const BArgs& a, dim3 grid, hipStream_t st) {
 // Work split.  The row steps of all distinct experts (GU: 32 rows of I, one
 // gate and up row per lane group; DN: 64 rows of H, two per lane group) are
 // laid end to end and cut into one contiguous range per workgroup of equal
-// cost, a row step of expert u costing passes_u * dm_costw(K) + 4 tokens_u
+// cost, a row step of expert u costing passes_u * dm_costw(GU, K) + 4 tokens_u
 // (weight bytes plus per-token work, in quarters of one token's work).  A workgroup walks its range expert by
 // expert; for each it stages the activations of up to ntp pairs in LDS
 // (fp32, 36 floats per 32 so the 16 lanes of a group hit distinct banks) and
@@ -983,8 +983,9 @@ constexpr int kDSC = 2;                    // 16-byte chunks per lane per pipeli
 constexpr int kDPipe = 3;                  // register buffers of the weight stream
 // One weight pass of a row step in quarters of a token's work on it (the
 // matrix-core products, their LDS operands and the epilogue): per-workgroup
-// clocks put a pass of a row step (64 rows of K) at about K / 580 tokens.
-__device__ __forceinline__ int dm_costw(int K) { return (4 * K + 290) / 580; }
+// clocks put a pass of a row step (64 rows of K) at about K / 270 tokens on
+// gate/up and K / 380 on down.
+__device__ __forceinline__ int dm_costw(bool GU, int K) { return GU ? (4 * K + 135) / 270 : (4 * K + 190) / 380; }
 constexpr int kDLds = 131072;              // LDS bytes for staged activations
 constexpr int kDMaxU = MOE_MAX_DECODE_TOKENS * MOE_MAX_TOPK;   // distinct experts at most
 
@@ -1310,7 +1311,7 @@ __global__ __launch_bounds__(kDWG) void k_dstream(DArgs a) {
 
   // cost prefix over the distinct experts, then this workgroup's range
   const int ntok = tid < CK ? a.disp[disp_untok(CK) + tid] : 0;   // loaded beside nu
-  const int wu = tid < nu ? ((ntok + ntp - 1) / ntp) * dm_costw(K) + 4 * ntok : 0;
+  const int wu = tid < nu ? ((ntok + ntp - 1) / ntp) * dm_costw(GU, K) + 4 * ntok : 0;
   int total = 0;
   const int pre = block_excl_scan_dwg(tid < nu ? wu * nrs : 0, s_w, &total);
   if (tid < nu) s_pref[tid] = pre;

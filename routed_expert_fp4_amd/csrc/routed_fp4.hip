@@ -335,6 +335,8 @@ __device__ void build_dispatch(TopkShared& S, int32_t* disp, int C, int k, int E
   }
 }
 
+constexpr int kRouteWt = 2048;           // router: most columns per x tile (8 float4 per lane)
+
 template <int CM>
 __global__ __launch_bounds__(kWG) void k_route(RouteArgs a) {
   __shared__ float xs[kRouteXs];
@@ -343,18 +345,29 @@ __global__ __launch_bounds__(kWG) void k_route(RouteArgs a) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
 
   if (a.x) {
-    constexpr int KT = kRouteXs / CM;          // x tile per token (floats)
+    // x tiles of KT columns per token (KT: a multiple of 256 that fits the
+    // call's C tokens in LDS, at most kRouteWt); each wave's row loads of a
+    // tile are issued before the tile is staged, so the two latencies overlap
+    const int KT = min(kRouteWt, (kRouteXs / a.C) & ~255);
     const int b = blockIdx.x;
     const int rbk = b / a.ksplit, ks = b - rbk * a.ksplit;
     const int e = rbk * 4 + wave;
     const int k0 = ks * a.kper;
     const int k1 = min(a.H, k0 + a.kper);
+    const float4* wrow = reinterpret_cast<const float4*>(a.Wr + (size_t)(e < a.E ? e : 0) * a.H);
     float acc[CM];
 #pragma unroll
     for (int t = 0; t < CM; ++t) acc[t] = 0.0f;
     for (int kt = k0; kt < k1; kt += KT) {
       const int kn = min(KT, k1 - kt);
-      __syncthreads();
+      const int n4 = kn >> 2;
+      float4 wv[kRouteWt / 256];
+#pragma unroll
+      for (int u = 0; u < kRouteWt / 256; ++u) {
+        const int c = lane + 64 * u;
+        wv[u] = (e < a.E && c < n4) ? wrow[(kt >> 2) + c] : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+      __syncthreads();                         // the previous tile's products are done
       for (int i = tid * 4; i < a.C * kn; i += kWG * 4) {
         const int t = i / kn, col = i - t * kn;
         *reinterpret_cast<float4*>(&xs[t * KT + col]) =
@@ -362,23 +375,16 @@ __global__ __launch_bounds__(kWG) void k_route(RouteArgs a) {
       }
       __syncthreads();
       if (e < a.E) {
-        const float4* wrow = reinterpret_cast<const float4*>(a.Wr + (size_t)e * a.H + kt);
         const float4* x4 = reinterpret_cast<const float4*>(xs);
-        const int n4 = kn >> 2;
-        for (int c = lane; c < n4; c += 64 * 4) {
-          float4 wv[4];
 #pragma unroll
-          for (int u = 0; u < 4; ++u)
-            if (c + 64 * u < n4) wv[u] = wrow[c + 64 * u];
+        for (int u = 0; u < kRouteWt / 256; ++u) {
+          const int c = lane + 64 * u;
+          if (c < n4) {
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            if (c + 64 * u < n4) {
-#pragma unroll
-              for (int t = 0; t < CM; ++t) {
-                if (t < a.C) {
-                  const float4 xv = x4[(t * KT >> 2) + c + 64 * u];
-                  acc[t] += wv[u].x * xv.x + wv[u].y * xv.y + wv[u].z * xv.z + wv[u].w * xv.w;
-                }
+            for (int t = 0; t < CM; ++t) {
+              if (t < a.C) {
+                const float4 xv = x4[(t * KT >> 2) + c];
+                acc[t] += wv[u].x * xv.x + wv[u].y * xv.y + wv[u].z * xv.z + wv[u].w * xv.w;
               }
             }
           }
