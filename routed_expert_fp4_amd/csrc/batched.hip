@@ -1344,7 +1344,7 @@ __global__ __launch_bounds__(kDWG) void k_dstream(DArgs a) {
       if (tid < nt) s_pairs[tid] = a.disp[disp_upair(CK) + u * a.C + p0 + tid];
       __syncthreads();
       // each activation as hi = bf16(v) and lo = bf16(v - hi) (v - hi is exact
-      // in fp32; hi + lo is v to within 2^-18 relative); the pair slot after
+      // in fp32; hi + lo is v to within 2^-17 relative); the pair slot after
       // an odd count is zero, so the last column group's second pair adds 0
       const int ntc = (nt + 1) & ~1;
       for (int q = tid * 4; q < ntc * K; q += kDWG * 4) {
