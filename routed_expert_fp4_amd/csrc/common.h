@@ -150,11 +150,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_view(const void* base
 __device__ __forceinline__ float coherent_ld(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
   return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)byte_off, 0, kCachePolicySc1));
 }
-__device__ __forceinline__ float4 coherent_ld4(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
-  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, kCachePolicySc1);
-  return make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]),
-                     __uint_as_float(v[3]));
-}
 // All of this workgroup's stores are complete, then one ticket; returns true
 // (in every thread) for the workgroup that drew ticket n-1.
 __device__ __forceinline__ bool last_to_arrive(uint32_t* ticket, uint32_t n, int* s_flag) {

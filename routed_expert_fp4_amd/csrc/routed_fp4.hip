@@ -176,63 +176,6 @@ __device__ void wave_topk(TopkShared& S, const uint32_t (&key)[16], const float 
   __syncthreads();
 }
 
-// Wave-wide max / min of a 32-bit value with DPP row shifts and row
-// broadcasts (lane 63 ends with the result; every lane receives it).
-template <bool MAX>
-__device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v) {
-  const int id = MAX ? 0 : -1;   // identity for lanes without a source
-  auto op = [](uint32_t a, uint32_t b) { return MAX ? (a > b ? a : b) : (a < b ? a : b); };
-  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x111, 0xF, 0xF, false));  // row_shr:1
-  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x112, 0xF, 0xF, false));  // row_shr:2
-  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x114, 0xF, 0xF, false));  // row_shr:4
-  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x118, 0xF, 0xF, false));  // row_shr:8
-  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x142, 0xA, 0xF, false));  // row_bcast:15
-  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x143, 0xC, 0xF, false));  // row_bcast:31
-  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
-}
-
-// Exact top-k of up to 64*N (key, index, logit) entries held N per lane by one
-// wave: each lane sorts its entries by (key desc, index asc), then k rounds
-// each take the best lane head (wave max of the keys; equal keys go to the
-// lowest index) and pop it.  Empty entries are (0, 0xFFFF).  Results land in
-// out_key / out_e / out_l [0, k) in rank order.
-template <int N>
-__device__ void wave_tournament(uint32_t (&key)[N], uint32_t (&ix)[N], float (&lv)[N], int k,
-                                uint32_t* out_key, int32_t* out_e, float* out_l) {
-  const int lane = threadIdx.x & 63;
-  // odd-even transposition sort of the lane's N entries (N is tiny)
-#pragma unroll
-  for (int pass = 0; pass < N; ++pass) {
-#pragma unroll
-    for (int i = pass & 1; i + 1 < N; i += 2) {
-      const bool sw = key[i] < key[i + 1] || (key[i] == key[i + 1] && ix[i] > ix[i + 1]);
-      const uint32_t k0 = sw ? key[i + 1] : key[i], k1 = sw ? key[i] : key[i + 1];
-      const uint32_t i0 = sw ? ix[i + 1] : ix[i], i1 = sw ? ix[i] : ix[i + 1];
-      const float l0 = sw ? lv[i + 1] : lv[i], l1 = sw ? lv[i] : lv[i + 1];
-      key[i] = k0; key[i + 1] = k1; ix[i] = i0; ix[i + 1] = i1; lv[i] = l0; lv[i + 1] = l1;
-    }
-  }
-  for (int s = 0; s < k; ++s) {
-    const uint32_t m = wave_reduce_u32<true>(key[0]);
-    const unsigned long long tied = __ballot(key[0] == m);
-    uint32_t we;
-    if (__popcll(tied) == 1) we = (uint32_t)__shfl((int)ix[0], __ffsll((long long)tied) - 1, 64);
-    else we = wave_reduce_u32<false>(key[0] == m ? ix[0] : 0xFFFFFFFFu);
-    const bool win = key[0] == m && ix[0] == we;
-    if (win) {
-      out_key[s] = m;
-      out_e[s] = (int32_t)we;
-      out_l[s] = lv[0];
-#pragma unroll
-      for (int i = 0; i + 1 < N; ++i) { key[i] = key[i + 1]; ix[i] = ix[i + 1]; lv[i] = lv[i + 1]; }
-      key[N - 1] = 0u;
-      ix[N - 1] = 0xFFFFu;
-      lv[N - 1] = 0.0f;
-    }
-  }
-  (void)lane;
-}
-
 // Top-k of token t by one wave of the router's last workgroup.
 __device__ void topk_token(const RouteArgs& a, TopkShared& S, int t, bool active) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -745,25 +688,6 @@ constexpr int kMaxI1 = 4096;
 constexpr int kXcds = 8;                   // XCDs; workgroup w is dispatched to XCD w % 8
 constexpr uint32_t kXcdPolls = 256;       // XCD-copy polls before the coherent copy
 constexpr uint32_t kSpinLimit = 1u << 22; // ~seconds: a wait that never ends gives up
-
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-
-// Weight bytes are read once per call: non-temporal loads keep them from
-// displacing the activations and hand-off data in the caches.
-__device__ __forceinline__ uint4 load_stream16(const uint8_t* p) {
-  const u32x4_t t = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
-  return make_uint4(t.x, t.y, t.z, t.w);
-}
-__device__ __forceinline__ float4 load_stream16f(const float* p) {
-  const f32x4_t t = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
-  return make_float4(t.x, t.y, t.z, t.w);
-}
-template <int FMT>
-__device__ __forceinline__ uint32_t load_scales_stream(const uint8_t* srow, int c) {
-  if (FMT == MOE_FMT_MXFP4) return __builtin_nontemporal_load(srow + c);
-  return __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(srow + 2 * c));
-}
 
 // (epoch, fp32) hand-off words
 __device__ __forceinline__ void store_tagged(uint64_t* p, uint32_t epoch, float v) {
