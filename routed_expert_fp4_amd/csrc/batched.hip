@@ -1219,7 +1219,7 @@ __device__ int block_excl_scan_dwg(int v, int* s_w, int* total) {
 template <int FMT, bool GU, int NTC>
 __device__ __forceinline__ void dstream_pass(const DArgs& a, const uint8_t* rec, int rsb, int rse,
                                              const uint8_t* xs, int ps, int ts, int nt,
-                                             const int* s_pairs) {
+                                             const int* s_pairs, const float* s_wgt) {
   const int H = a.H, I = a.I, K = GU ? H : I;
   const int B = (FMT == MOE_FMT_MXFP4) ? 32 : 16;
   constexpr int RS = GU ? kDGrp : 2 * kDGrp;          // rows per row step
@@ -1284,7 +1284,7 @@ __device__ __forceinline__ void dstream_pass(const DArgs& a, const uint8_t* rec,
         const int t = 2 * g + tw;
         if (writer && t < nt) {
           const int p = s_pairs[t];
-          const float wp = a.w[p] * gd;
+          const float wp = s_wgt[t] * gd;               // routing weight, staged with the pairs
           a.part[(size_t)p * H + j] = wp * y0;
           a.part[(size_t)p * H + j + kDGrp] = wp * y1;
         }
@@ -1300,6 +1300,7 @@ __global__ __launch_bounds__(kDWG) void k_dstream(DArgs a) {
   __shared__ int s_w[kDWG / 64];
   __shared__ int s_bound[2];
   __shared__ int s_pairs[MOE_MAX_DECODE_TOKENS];
+  __shared__ float s_wgt[MOE_MAX_DECODE_TOKENS];      // down: the pairs' routing weights
   const int tid = threadIdx.x;
   const int CK = a.C * a.k;
   const int nu = a.disp[0];
@@ -1341,7 +1342,11 @@ __global__ __launch_bounds__(kDWG) void k_dstream(DArgs a) {
     for (int p0 = 0; p0 < nt_u; p0 += ntp) {
       const int nt = min(ntp, nt_u - p0);
       __syncthreads();                                  // the previous pass is done with LDS
-      if (tid < nt) s_pairs[tid] = a.disp[disp_upair(CK) + u * a.C + p0 + tid];
+      if (tid < nt) {
+        const int p = a.disp[disp_upair(CK) + u * a.C + p0 + tid];
+        s_pairs[tid] = p;
+        if (!GU) s_wgt[tid] = a.w[p];
+      }
       __syncthreads();
       // each activation as hi = bf16(v) and lo = bf16(v - hi) (v - hi is exact
       // in fp32; hi + lo is v to within 2^-17 relative); the pair slot after
@@ -1365,9 +1370,9 @@ __global__ __launch_bounds__(kDWG) void k_dstream(DArgs a) {
       __syncthreads();
       // the smallest instance that holds the pass, so that no column group
       // past its pairs is multiplied
-      if (NT <= 2 || nt <= 2) dstream_pass<FMT, GU, 2>(a, rec, rsb, rse, xs, ps, ts, nt, s_pairs);
-      else if (NT == 4 || nt <= 4) dstream_pass<FMT, GU, 4>(a, rec, rsb, rse, xs, ps, ts, nt, s_pairs);
-      else dstream_pass<FMT, GU, 8>(a, rec, rsb, rse, xs, ps, ts, nt, s_pairs);
+      if (NT <= 2 || nt <= 2) dstream_pass<FMT, GU, 2>(a, rec, rsb, rse, xs, ps, ts, nt, s_pairs, s_wgt);
+      else if (NT == 4 || nt <= 4) dstream_pass<FMT, GU, 4>(a, rec, rsb, rse, xs, ps, ts, nt, s_pairs, s_wgt);
+      else dstream_pass<FMT, GU, 8>(a, rec, rsb, rse, xs, ps, ts, nt, s_pairs, s_wgt);
     }
   }
 }
