@@ -150,14 +150,20 @@ def test_route_logits_in_bit_exact(E, k, C, seed):
     np.testing.assert_allclose(w.cpu().numpy(), wr, rtol=2e-6, atol=1e-7)
 
 
-def test_route_logits_in_all_equal_and_nan():
-    say("[route logits-in] adversarial")
-    E, k, C = 40, 6, 3
+@pytest.mark.parametrize("C", [3, 20])
+def test_route_logits_in_all_equal_and_nan(C):
+    """All-equal rows, NaN and -inf logits; C = 20 takes the many-token top-k
+    launch (one wave per token), whose candidate gather falls back to
+    rounds of the wave maximum when more than 64 entries tie."""
+    say(f"[route logits-in] adversarial C={C}")
+    E, k = 40, 6
     L = np.zeros((C, E), np.float32)
     L[1] = np.linspace(-1, 1, E, dtype=np.float32)
     L[1, [3, 9]] = np.nan
     L[2] = -np.inf
     L[2, 7] = 0.5
+    for t in range(3, C):                      # the three patterns again, shifted
+        L[t] = np.roll(L[t % 3], t)
     idx = torch.empty((C, k), dtype=torch.int32, device="cuda")
     w = torch.empty((C, k), dtype=torch.float32, device="cuda")
     rf().moe_route(None, None, to_dev(L), C, 32, E, k, idx, w, _ws(E, 32, 32, k, C))
