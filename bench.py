@@ -183,7 +183,8 @@ def expert_bytes(spec) -> int:
     return spec.expert_bytes()
 
 
-def cpu_baseline(wl, layers: int, max_tokens: int = 8, threads: int = 0, max_experts: int = 0):
+def cpu_baseline(wl, layers: int, max_tokens: int = 8, threads: int = 0, max_experts: int = 0,
+                 keep: dict = None):
     """The oracle as it is, on `layers` layer calls of the workload with at
     most `max_tokens` tokens each (the first tokens of the call); input
     regeneration (the synthetic bank bytes) is excluded from the timing.  Each
@@ -191,7 +192,9 @@ def cpu_baseline(wl, layers: int, max_tokens: int = 8, threads: int = 0, max_exp
     oracle's OpenMP threads (0: all it has).  max_experts > 0 times only the
     first max_experts distinct experts of each call and scales their time by
     the call's (token, slot) pairs over the sampled experts' pairs (the
-    router, top-k, weights and combine are timed whole)."""
+    router, top-k, weights and combine are timed whole).  keep (a dict): with
+    every expert computed, receives layer 0's inputs and oracle outputs (x,
+    Wr, idx, out) for the parity sample."""
     import numpy as np
     import oracle
     import synth
@@ -231,10 +234,10 @@ def cpu_baseline(wl, layers: int, max_tokens: int = 8, threads: int = 0, max_exp
                     pairs += 1
             t_exp = (time.perf_counter() - t1) * (C * wl.k / pairs)
             t2 = time.perf_counter()
-            for tok in range(C):
-                w = oracle.route_weights(L[tok, idx[tok]])
-                oracle.combine(w, ys[tok])
+            outs = [oracle.combine(oracle.route_weights(L[tok, idx[tok]]), ys[tok]) for tok in range(C)]
             total += t_route + t_exp + (time.perf_counter() - t2)
+            if keep is not None and l == 0 and not max_experts:
+                keep.update(x=x, Wr=Wr, idx=idx, out=np.stack(outs))
             sampled.append(len(take))
         cores = int(L_.orc_threads())
     finally:
@@ -252,6 +255,34 @@ def cpu_baseline(wl, layers: int, max_tokens: int = 8, threads: int = 0, max_exp
     sample += "and the combine; bank byte regeneration not timed"
     return {"value": us, "unit": "us/token per MoE layer", "cores": cores,
             "kind": "oracle", "sample": sample}
+
+
+def parity_sample(rf, bank, ref, wl, ws, dev):
+    """The timed path on the oracle's own sample (layer 0, pool draw 0, the
+    call's tokens): outputs against the fp64 oracle at the library's bar, and
+    the tokens whose selection equals the oracle's (a token that differs is a
+    near-tie only if the tests' certified bound allows it; here it is just
+    counted)."""
+    import numpy as np
+    import torch
+    import oracle
+    C = ref["x"].shape[0]
+    x = torch.from_numpy(np.ascontiguousarray(ref["x"])).to(dev)
+    Wr = torch.from_numpy(np.ascontiguousarray(ref["Wr"])).to(dev)
+    out = torch.empty((C, wl.H), dtype=torch.float32, device=dev)
+    idx = torch.empty((C, wl.k), dtype=torch.int32, device=dev)
+    rf.moe_layer_fwd(bank, Wr, x, C, wl.k, out, topk_idx_out=idx, ws=ws)
+    torch.cuda.synchronize()
+    check_error_word(ws, "parity sample")
+    got = out.cpu().numpy()
+    r, m = oracle.rel_l2(got, ref["out"]), oracle.max_abs_ratio(got, ref["out"])
+    same = int(np.sum(np.all(idx.cpu().numpy() == ref["idx"], axis=1)))
+    return {"rel_l2": float(f"{r:.3e}"), "max_abs_ratio": float(f"{m:.3e}"),
+            "tokens": C, "tokens_with_oracle_selection": same,
+            "within_bar": bool(r <= 2e-5 and m <= 1e-4),
+            "bar": "rel-L2 <= 2e-5 and max-abs <= 1e-4 x max|ref| (the tests' bar)",
+            "sample": "layer 0, pool draw 0, the call's tokens, through moe_layer_fwd, "
+                      "against the fp64 CPU oracle"}
 
 
 def cpu_baseline_latent(wl):
@@ -505,6 +536,19 @@ def main():
     wall = time.perf_counter() - t0
     check_error_word(ws, "layer timing")
     ms_step = e0.elapsed_time(e1) / args.steps
+    # one layer call alone, the stream idle before it (events around the call)
+    singles = []
+    if not args.mx_mma:
+        for r in range(7):
+            j = r % pool
+            torch.cuda.synchronize()
+            a1, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a1.record(stream)
+            rf.moe_layer_fwd(banks[0], wrs[0], xs[0][j * C:(j + 1) * C], C, wl.k, outs[0], ws=ws)
+            b1.record(stream)
+            torch.cuda.synchronize()
+            singles.append(a1.elapsed_time(b1) * 1000.0)
+        check_error_word(ws, "single-call timing")
     us_call = ms_step * 1000.0 / wl.layers          # one moe_layer_fwd call (C tokens)
     us_layer = us_call / C                          # per token per MoE layer
 
@@ -593,6 +637,7 @@ def main():
                    "layers": wl.layers, "experts": wl.E, "top_k": wl.k, "hidden": wl.H,
                    "inter": wl.I, "format": fmt, "tokens_per_call": C},
         "us_per_call": round(us_call, 3),
+        "us_single_call": round(float(np.median(singles)), 3) if singles else None,
         "hbm_gbps_selected_expert_bytes": round(gbps_layer, 1),
         "hbm_frac_of_peak": round(gbps_layer / HBM_PEAK_GBPS, 4),
         "tokens_per_s": round(1000.0 * C / ms_step, 2),
@@ -619,7 +664,10 @@ def main():
         result["roofline"]["frac_of_single_launch_read"] = round(gbps_kernel / single, 4)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle ...")
-        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_layers)
+        ref = {}
+        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_layers, keep=ref)
+        if ref and ref["x"].shape[0] == C and not args.mx_mma:
+            result["parity_sample"] = parity_sample(rf, banks[0], ref, wl, ws, dev)
         log("timing the CPU oracle on one core (sampled experts) ...")
         result["cpu_baseline_1core"] = cpu_baseline(wl, 1, threads=1,
                                                     max_experts=2 if wl.C == 1 else 4)
