@@ -285,11 +285,12 @@ def parity_sample(rf, bank, ref, wl, ws, dev):
                       "against the fp64 CPU oracle"}
 
 
-def cpu_baseline_latent(wl):
+def cpu_baseline_latent(wl, keep: dict = None):
     """The oracle as it is on one token of the latent workload's first layer:
     router, routed_down, dequantisation and FFN of each selected routed expert,
     the combine, the norm, routed_up and the shared experts; bank byte
-    regeneration (synth) is done before the timing."""
+    regeneration (synth) is done before the timing.  keep (a dict) receives
+    the token, the oracle's selection and output for the parity sample."""
     import numpy as np
     import oracle
     import synth
@@ -309,8 +310,10 @@ def cpu_baseline_latent(wl):
     t0 = time.perf_counter()
     rc = {e: deq(rs, t) for e, t in rt.items()}
     sc = {j: deq(ss, t) for j, t in st.items()}
-    oracle.latent_layer(wl, Wr, x, Wd, Wu, g, routed_cache=rc, shared_cache=sc)
+    ref = oracle.latent_layer(wl, Wr, x, Wd, Wu, g, routed_cache=rc, shared_cache=sc)
     us = (time.perf_counter() - t0) * 1e6
+    if keep is not None:
+        keep.update(x=x, idx=idx, out=ref["out"])
     return {"value": us, "unit": "us/token per latent MoE layer",
             "cores": int(oracle.lib().orc_threads()), "kind": "oracle",
             "sample": "1 token of layer 0 (pool draw 0): dequantisation of the selected routed "
@@ -418,7 +421,25 @@ def bench_latent(args, wl):
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle ...")
-        result["cpu_baseline"] = cpu_baseline_latent(wl)
+        ref = {}
+        result["cpu_baseline"] = cpu_baseline_latent(wl, keep=ref)
+        if ref and C == ref["x"].shape[0]:
+            import oracle
+            xg = torch.from_numpy(np.ascontiguousarray(ref["x"])).to(dev)
+            og = torch.empty((C, wl.H), dtype=torch.float32, device=dev)
+            ig = torch.empty((C, wl.k), dtype=torch.int32, device=dev)
+            rf.moe_latent_layer_fwd(layers[0], xg, C, wl.k, og, ig, None, ws)
+            torch.cuda.synchronize()
+            check_error_word(ws, "parity sample")
+            got = og.cpu().numpy()
+            r, m = oracle.rel_l2(got, ref["out"]), oracle.max_abs_ratio(got, ref["out"])
+            result["parity_sample"] = {
+                "rel_l2": float(f"{r:.3e}"), "max_abs_ratio": float(f"{m:.3e}"), "tokens": C,
+                "tokens_with_oracle_selection": int(np.sum(np.all(ig.cpu().numpy() == ref["idx"], axis=1))),
+                "within_bar": bool(r <= 2e-5 and m <= 1e-4),
+                "bar": "rel-L2 <= 2e-5 and max-abs <= 1e-4 x max|ref| (the tests' bar)",
+                "sample": "layer 0, pool draw 0, one token, through moe_latent_layer_fwd, "
+                          "against the fp64 CPU oracle"}
     print(json.dumps(result), flush=True)
 
 
