@@ -571,16 +571,6 @@ __global__ __launch_bounds__(256) void k_brouter(const float* x, const float* Wr
   }
 }
 
-// One wave per token: the decode path's exact top-k and renormalised sigmoid
-// weights.  The logits are given, or are the sums of ksplit partial sums
-// lpart[s][t][e], added in split order (and then stored to logits_out if
-// that is not null).
-// One wave per token.  With `disp`, all C <= 16 tokens are in this one
-// workgroup (1024 threads) and it also writes the dispatch table: distinct
-// experts in order of first use (pair order), each with its pairs in token
-// order.  A router selection names distinct experts per token, so the pairs
-// of expert e are marked by a token bitmask and a pair's place in the list is
-// the number of earlier tokens in the mask.
 // The same exact top-k as wave_select (same keys, same result), with fewer
 // steps for the usual case, as the single-launch decode kernel selects: T is
 // the largest 16-bit key prefix that at least k lane maxima reach (a 16-step
@@ -640,6 +630,15 @@ __device__ void wave_select_fast(uint64_t (&ck)[NPL], const float (&lv)[NPL], in
   wave_lds_fence();
 }
 
+// One wave per token: the decode path's exact top-k and renormalised sigmoid
+// weights.  The logits are given, or are the sums of ksplit partial sums
+// lpart[s][t][e], added in split order (and then stored to logits_out if
+// that is not null).  With `disp`, all C <= 16 tokens are in this one
+// workgroup (1024 threads) and it also writes the dispatch table: distinct
+// experts in order of first use (pair order), each with its pairs in token
+// order.  A router selection names distinct experts per token, so the pairs
+// of expert e are marked by a token bitmask and a pair's place in the list is
+// the number of earlier tokens in the mask.
 template <int NW>
 __global__ __launch_bounds__(64 * NW) void k_btopk(const float* logits, const float* lpart, int ksplit,
                                                    float* logits_out, int C, int E, int k,
