@@ -33,9 +33,9 @@
 //   k_bscan     offsets and the tile list (each expert's pairs in tiles of
 //               16 or 64)
 //   k_bscatter  pairs grouped by expert
-//   k_bmm<GU>   per (tile, 64 rows of I): gate and up on MFMA, SwiGLU, h as
+//   k_bmm<GU>   per (tile, 256 rows of I): gate and up on MFMA, SwiGLU, h as
 //               two bf16 planes
-//   k_bmm<DN>   per (tile, 128 rows of H): down on MFMA, times the routing
+//   k_bmm<DN>   per (tile, 512 rows of H): down on MFMA, times the routing
 //               weight, one fp32 row per pair
 //   k_bcombine  out[t] = sum of its pairs' rows in slot order (deterministic)
 // and for the router of many tokens:
@@ -52,8 +52,10 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kRmGU = 1;             // gate/up: 16-row MFMA tiles per wave (64 rows per workgroup)
-constexpr int kRmDN = 2;             // down: 16-row MFMA tiles per wave (128 rows per workgroup)
+constexpr int kRmGU = 1;             // gate/up: 16-row MFMA tiles per wave
+constexpr int kRmDN = 2;             // down: 16-row MFMA tiles per wave
+constexpr int kNwGU = 16;            // gate/up: waves per workgroup (256 rows of each matrix)
+constexpr int kNwDN = 16;            // down: waves per workgroup (512 rows)
 constexpr int kRmGUn = 2;            // narrow tiles: gate/up 128 rows per workgroup
 constexpr int kRmDNn = 4;            // narrow tiles: down 256 rows per workgroup
 constexpr int kRK = 32;              // router: K elements per staged chunk
@@ -222,9 +224,12 @@ __global__ __launch_bounds__(256) void k_bscatter(BArgs a) {
 // Grouped GEMMs
 // ---------------------------------------------------------------------------
 // k_bmm: one grouped GEMM (gate/up with SwiGLU, or down) for one tile of up
-// to NTOK = 16 * NB pairs of one expert and 64 * RM rows of each of NMAT
-// weight matrices (wave w owns rows 16 RM w .. 16 RM w + 16 RM - 1, as RM
-// MFMA row tiles).
+// to NTOK = 16 * NB pairs of one expert and 16 * RM * NW rows of each of NMAT
+// weight matrices (wave w of NW owns rows 16 RM w .. 16 RM w + 16 RM - 1, as
+// RM MFMA row tiles).  Sixteen waves share one staged activation tile, so
+// the tile's reads from L2 per weight byte are a quarter of what four waves
+// need (at four they matched the weight bytes), and the 128-register limit
+// of a 1024-thread workgroup still gives one workgroup of 16 waves per CU.
 //
 // K runs in stages of 256 elements: lane l of a wave reads 32 contiguous code
 // bytes of row (l % 16) of each row tile, at K offset 64 (l / 16) of the
@@ -282,22 +287,22 @@ __device__ __forceinline__ void load_stage(const __amdgpu_buffer_rsrc_t (&codes)
   }
 }
 
-template <int NTOK, int PL>
+template <int NTOK, int PL, int NTHR>
 struct StageB {
-  uint4 v[PL][NTOK / 8];                 // PL planes of NTOK rows x 256 bf16 / 256 threads
+  uint4 v[PL][NTOK * 32 / NTHR];         // PL planes of NTOK rows x 256 bf16 / NTHR threads
 };
 
 // Activation stage kb, planes pl0 .. pl0+PL-1 (those below np), of the tile's
 // first `rows` rows (rows past cnt read as zero) into registers.
-template <int NTOK, int PL>
+template <int NTOK, int PL, int NTHR>
 __device__ __forceinline__ void load_b(__amdgpu_buffer_rsrc_t src, uint32_t plane_bytes, int row_elems,
                                        const int* s_row, int cnt, int pl0, int np, int kb,
-                                       StageB<NTOK, PL>& B) {
+                                       StageB<NTOK, PL, NTHR>& B) {
 #pragma unroll
   for (int pl = 0; pl < PL; ++pl)
 #pragma unroll
-    for (int u = 0; u < NTOK / 8; ++u) {
-      const int q = threadIdx.x + 256 * u, c = q >> 5, ch = q & 31;
+    for (int u = 0; u < NTOK * 32 / NTHR; ++u) {
+      const int q = threadIdx.x + NTHR * u, c = q >> 5, ch = q & 31;
       const bool ok = c < cnt && pl0 + pl < np;
       const uint32_t off = ok ? (uint32_t)(pl0 + pl) * plane_bytes +
                                     ((uint32_t)s_row[c] * row_elems + kb * kSK + ch * 8) * 2u
@@ -309,13 +314,13 @@ __device__ __forceinline__ void load_b(__amdgpu_buffer_rsrc_t src, uint32_t plan
 
 // Every row is stored (rows past the tile's pairs hold zeros): a store under a
 // branch would cost the compiler its exact count of outstanding loads.
-template <int NTOK, int PL>
-__device__ __forceinline__ void store_b(uint16_t (*xs)[NTOK][kSStride], const StageB<NTOK, PL>& B) {
+template <int NTOK, int PL, int NTHR>
+__device__ __forceinline__ void store_b(uint16_t (*xs)[NTOK][kSStride], const StageB<NTOK, PL, NTHR>& B) {
 #pragma unroll
   for (int pl = 0; pl < PL; ++pl)
 #pragma unroll
-    for (int u = 0; u < NTOK / 8; ++u) {
-      const int q = threadIdx.x + 256 * u, c = q >> 5, ch = q & 31;
+    for (int u = 0; u < NTOK * 32 / NTHR; ++u) {
+      const int q = threadIdx.x + NTHR * u, c = q >> 5, ch = q & 31;
       *reinterpret_cast<uint4*>(&xs[pl][c][ch * 8]) = B.v[pl][u];
     }
 }
@@ -361,10 +366,12 @@ __device__ __forceinline__ void mfma_stage(const StageW<FMT, NMAT, RM>& W,
 // NB column tiles of 16 pairs at most (the tile's own count decides how many
 // run); PL activation planes staged per K stage (both h planes at once; x
 // planes one group at a time for wide tiles, whose x is usually bf16-exact).
-template <int FMT, bool GU, int RM, int NB>
-__global__ __launch_bounds__(256) void k_bmm(BArgs a) {
+template <int FMT, bool GU, int RM, int NB, int NW>
+__global__ __launch_bounds__(64 * NW) void k_bmm(BArgs a) {
   constexpr int NMAT = GU ? 2 : 1;
   constexpr int NTOK = 16 * NB;
+  constexpr int NTHR = 64 * NW;
+  static_assert(NTOK * 32 % NTHR == 0, "activation stage split");
   constexpr int PL = GU ? (NB == 1 ? 3 : 1) : 2;   // h: both planes at once
   __shared__ __attribute__((aligned(16))) uint16_t xs[PL][NTOK][kSStride];
   __shared__ int s_pair[NTOK], s_row[NTOK], s_flags;
@@ -391,7 +398,7 @@ __global__ __launch_bounds__(256) void k_bmm(BArgs a) {
   const int wave = tid >> 6, lane = tid & 63, g = lane >> 4, r16 = lane & 15;
   const int H = a.H, I = a.I, B = (FMT == MOE_FMT_MXFP4) ? 32 : 16;
   const int K = GU ? H : I, N = GU ? I : H;
-  const int row0 = blockIdx.x * (64 * RM) + wave * (16 * RM);
+  const int row0 = blockIdx.x * (16 * RM * NW) + wave * (16 * RM);
   const uint8_t* rec = a.base + (size_t)e * a.stride;
   __amdgpu_buffer_rsrc_t codes[NMAT], scales[NMAT];
   const uint32_t cbytes = (uint32_t)N * (K / 2), sbytes = (uint32_t)N * (K / B);
@@ -433,20 +440,20 @@ __global__ __launch_bounds__(256) void k_bmm(BArgs a) {
   for (int gr = 0; gr < ngr; ++gr) {
     const int pl0 = gr * PL, npl = min(PL, np - pl0);
     StageW<FMT, NMAT, RM> W0, W1;
-    StageB<NTOK, PL> B0, B1;
+    StageB<NTOK, PL, NTHR> B0, B1;
     load_stage<FMT, NMAT, RM>(codes, scales, coff, soff, 0, true, W0);
-    load_b<NTOK, PL>(src, plane_bytes, K, s_row, cnt, pl0, np, 0, B0);
+    load_b<NTOK, PL, NTHR>(src, plane_bytes, K, s_row, cnt, pl0, np, 0, B0);
     load_stage<FMT, NMAT, RM>(codes, scales, coff, soff, 1, true, W1);
     for (int kb = 0; kb < nkb; kb += 2) {
       __syncthreads();                         // the previous stage's LDS reads are done
-      store_b<NTOK, PL>(xs, B0);
-      load_b<NTOK, PL>(src, plane_bytes, K, s_row, cnt, pl0, np, kb + 1, B1);
+      store_b<NTOK, PL, NTHR>(xs, B0);
+      load_b<NTOK, PL, NTHR>(src, plane_bytes, K, s_row, cnt, pl0, np, kb + 1, B1);
       __syncthreads();
       mfma_stage<FMT, NMAT, RM, NB, NTOK, PL>(W0, xs, npl, nbr, acc);
       load_stage<FMT, NMAT, RM>(codes, scales, coff, soff, kb + 2, kb + 2 < nkb, W0);
       __syncthreads();
-      store_b<NTOK, PL>(xs, B1);
-      load_b<NTOK, PL>(src, plane_bytes, K, s_row, kb + 2 < nkb ? cnt : 0, pl0, np, kb + 2, B0);
+      store_b<NTOK, PL, NTHR>(xs, B1);
+      load_b<NTOK, PL, NTHR>(src, plane_bytes, K, s_row, kb + 2 < nkb ? cnt : 0, pl0, np, kb + 2, B0);
       __syncthreads();
       mfma_stage<FMT, NMAT, RM, NB, NTOK, PL>(W1, xs, npl, nbr, acc);
       load_stage<FMT, NMAT, RM>(codes, scales, coff, soff, kb + 3, kb + 3 < nkb, W1);
@@ -1487,7 +1494,7 @@ moe_status launch_batched_experts(const moe_bank* b, const float* x, int C, int 
   hipLaunchKernelGGL(k_bcount, dim3((CK + 255) / 256), dim3(256), 0, st, a);
   hipLaunchKernelGGL(k_bscan, dim3(1), dim3(1024), 0, st, a);
   hipLaunchKernelGGL(k_bscatter, dim3((CK + 255) / 256), dim3(256), 0, st, a);
-  const dim3 ggu(I / (64 * kRmGU), maxt), gdn(H / (64 * kRmDN), maxt);
+  const dim3 ggu(I / (16 * kRmGU * kNwGU), maxt), gdn(H / (16 * kRmDN * kNwDN), maxt);
   const dim3 ggun(I / (64 * kRmGUn), maxt), gdnn(H / (64 * kRmDNn), maxt);
 #define RF4_BMM(F)                                                                        \
   do {                                                                                    \
@@ -1496,8 +1503,8 @@ moe_status launch_batched_experts(const moe_bank* b, const float* x, int C, int 
       if (m == MOE_OK) m = launch_bdma<F, false, kRmDNn>(a, gdnn, st);                    \
       if (m != MOE_OK) return m;                                                          \
     } else {                                                                              \
-      hipLaunchKernelGGL((k_bmm<F, true, kRmGU, 4>), ggu, dim3(256), 0, st, a);           \
-      hipLaunchKernelGGL((k_bmm<F, false, kRmDN, 4>), gdn, dim3(256), 0, st, a);          \
+      hipLaunchKernelGGL((k_bmm<F, true, kRmGU, 4, kNwGU>), ggu, dim3(64 * kNwGU), 0, st, a); \
+      hipLaunchKernelGGL((k_bmm<F, false, kRmDN, 4, kNwDN>), gdn, dim3(64 * kNwDN), 0, st, a); \
     }                                                                                     \
   } while (0)
   if (b->format == MOE_FMT_MXFP4) RF4_BMM(MOE_FMT_MXFP4);
