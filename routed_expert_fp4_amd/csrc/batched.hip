@@ -373,7 +373,9 @@ __global__ __launch_bounds__(64 * NW) void k_bmm(BArgs a) {
   constexpr int NTHR = 64 * NW;
   static_assert(NTOK * 32 % NTHR == 0, "activation stage split");
   constexpr int PL = GU ? (NB == 1 ? 3 : 1) : 2;   // h: both planes at once
-  __shared__ __attribute__((aligned(16))) uint16_t xs[PL][NTOK][kSStride];
+  extern __shared__ __attribute__((aligned(16))) uint8_t bmm_lds[];   // two activation stages
+  uint16_t (*const xs0)[NTOK][kSStride] = reinterpret_cast<uint16_t (*)[NTOK][kSStride]>(bmm_lds);
+  uint16_t (*const xs1)[NTOK][kSStride] = xs0 + PL;
   __shared__ int s_pair[NTOK], s_row[NTOK], s_flags;
   const int tile = blockIdx.y;
   if (tile >= (int)a.meta[0]) return;
@@ -431,32 +433,36 @@ __global__ __launch_bounds__(64 * NW) void k_bmm(BArgs a) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) acc[m][r][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // K stages in pairs (nkb is even): buffers W0/B0 serve even stages, W1/B1
-  // odd ones, so a buffer is reloaded in place after use and no register copy
-  // of an in-flight load is ever needed (a copy would wait for the load).
-  // Plane groups beyond the first (wide tiles of non-bf16-exact x only)
-  // stream the weights again.
+  // K stages in pairs (nkb is even): weight buffer W0 and LDS stage xs0 serve
+  // even stages, W1 and xs1 odd ones, so a weight buffer is reloaded in place
+  // after use and no register copy of an in-flight load is ever needed (a
+  // copy would wait for the load).  The activations of stage kb + 1 go from
+  // registers into the other LDS stage before stage kb's products, whose
+  // reads of that stage (kb - 1) ended at the previous barrier: one barrier
+  // per stage.  Plane groups beyond the first (wide tiles of non-bf16-exact
+  // x only) stream the weights again.
   const int nkb = K / kSK;
   for (int gr = 0; gr < ngr; ++gr) {
     const int pl0 = gr * PL, npl = min(PL, np - pl0);
     StageW<FMT, NMAT, RM> W0, W1;
-    StageB<NTOK, PL, NTHR> B0, B1;
+    StageB<NTOK, PL, NTHR> Bs;
     load_stage<FMT, NMAT, RM>(codes, scales, coff, soff, 0, true, W0);
-    load_b<NTOK, PL, NTHR>(src, plane_bytes, K, s_row, cnt, pl0, np, 0, B0);
+    load_b<NTOK, PL, NTHR>(src, plane_bytes, K, s_row, cnt, pl0, np, 0, Bs);
     load_stage<FMT, NMAT, RM>(codes, scales, coff, soff, 1, true, W1);
+    store_b<NTOK, PL, NTHR>(xs0, Bs);
+    load_b<NTOK, PL, NTHR>(src, plane_bytes, K, s_row, cnt, pl0, np, 1, Bs);
+    __syncthreads();
     for (int kb = 0; kb < nkb; kb += 2) {
-      __syncthreads();                         // the previous stage's LDS reads are done
-      store_b<NTOK, PL, NTHR>(xs, B0);
-      load_b<NTOK, PL, NTHR>(src, plane_bytes, K, s_row, cnt, pl0, np, kb + 1, B1);
-      __syncthreads();
-      mfma_stage<FMT, NMAT, RM, NB, NTOK, PL>(W0, xs, npl, nbr, acc);
+      store_b<NTOK, PL, NTHR>(xs1, Bs);
+      load_b<NTOK, PL, NTHR>(src, plane_bytes, K, s_row, kb + 2 < nkb ? cnt : 0, pl0, np, kb + 2, Bs);
+      mfma_stage<FMT, NMAT, RM, NB, NTOK, PL>(W0, xs0, npl, nbr, acc);
       load_stage<FMT, NMAT, RM>(codes, scales, coff, soff, kb + 2, kb + 2 < nkb, W0);
       __syncthreads();
-      store_b<NTOK, PL, NTHR>(xs, B1);
-      load_b<NTOK, PL, NTHR>(src, plane_bytes, K, s_row, kb + 2 < nkb ? cnt : 0, pl0, np, kb + 2, B0);
-      __syncthreads();
-      mfma_stage<FMT, NMAT, RM, NB, NTOK, PL>(W1, xs, npl, nbr, acc);
+      store_b<NTOK, PL, NTHR>(xs0, Bs);        // stage kb + 2 (zeros past the last)
+      load_b<NTOK, PL, NTHR>(src, plane_bytes, K, s_row, kb + 3 < nkb ? cnt : 0, pl0, np, kb + 3, Bs);
+      mfma_stage<FMT, NMAT, RM, NB, NTOK, PL>(W1, xs1, npl, nbr, acc);
       load_stage<FMT, NMAT, RM>(codes, scales, coff, soff, kb + 3, kb + 3 < nkb, W1);
+      __syncthreads();
     }
   }
 
@@ -940,6 +946,23 @@ __global__ __launch_bounds__(256) void k_bdma(BArgs a) {
           make_float4(wp * acc[0][r][0][0], wp * acc[0][r][0][1], wp * acc[0][r][0][2],
                       wp * acc[0][r][0][3]);
   }
+}
+
+template <int FMT, bool GU, int RM, int NB, int NW>
+moe_status launch_bmm(const BArgs& a, dim3 grid, hipStream_t st) {
+  constexpr int PL = GU ? (NB == 1 ? 3 : 1) : 2;
+  constexpr int bytes = 2 * PL * 16 * NB * kSStride * 2;
+  static std::atomic<bool> attr_set[64];   // per device, set once (concurrent setters agree)
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (!attr_set[dev].load(std::memory_order_relaxed)) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(k_bmm<FMT, GU, RM, NB, NW>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, bytes) != hipSuccess)
+      return MOE_ERR_DEVICE;
+    attr_set[dev].store(true, std::memory_order_relaxed);
+  }
+  hipLaunchKernelGGL((k_bmm<FMT, GU, RM, NB, NW>), grid, dim3(64 * NW), bytes, st, a);
+  return MOE_OK;
 }
 
 template <int FMT, bool GU, int RM>
@@ -1503,8 +1526,9 @@ moe_status launch_batched_experts(const moe_bank* b, const float* x, int C, int 
       if (m == MOE_OK) m = launch_bdma<F, false, kRmDNn>(a, gdnn, st);                    \
       if (m != MOE_OK) return m;                                                          \
     } else {                                                                              \
-      hipLaunchKernelGGL((k_bmm<F, true, kRmGU, 4, kNwGU>), ggu, dim3(64 * kNwGU), 0, st, a); \
-      hipLaunchKernelGGL((k_bmm<F, false, kRmDN, 4, kNwDN>), gdn, dim3(64 * kNwDN), 0, st, a); \
+      moe_status m = launch_bmm<F, true, kRmGU, 4, kNwGU>(a, ggu, st);                    \
+      if (m == MOE_OK) m = launch_bmm<F, false, kRmDN, 4, kNwDN>(a, gdn, st);             \
+      if (m != MOE_OK) return m;                                                          \
     }                                                                                     \
   } while (0)
   if (b->format == MOE_FMT_MXFP4) RF4_BMM(MOE_FMT_MXFP4);
