@@ -44,6 +44,7 @@
 #include "common.h"
 
 #include <atomic>
+#include <type_traits>
 
 namespace rf4 {
 namespace {
@@ -326,11 +327,16 @@ __device__ __forceinline__ void store_b(uint16_t (*xs)[NTOK][kSStride], const St
 }
 
 // One K stage: for each MFMA step the weights are dequantised once and used
-// for the nbr (<= NB) column tiles and npl (<= PL) staged planes.
-template <int FMT, int NMAT, int RM, int NB, int NTOK, int PL>
+// for the column tiles that hold pairs and the PL staged planes.  Without
+// DYN their count NBR (<= NB) is a compile-time constant, so the steps hold
+// no branches and the compiler can move a step's LDS reads and
+// dequantisation ahead of the previous step's products; with DYN the count
+// is the runtime nbr (a branch per column tile, fewer registers live).
+template <int FMT, int NMAT, int RM, int NB, int NTOK, int PL, int NBR, bool DYN>
 __device__ __forceinline__ void mfma_stage(const StageW<FMT, NMAT, RM>& W,
-                                           const uint16_t (*xs)[NTOK][kSStride], int npl, int nbr,
+                                           const uint16_t (*xs)[NTOK][kSStride], int nbr,
                                            f32x4_t (&acc)[NMAT][RM][NB]) {
+  static_assert(NBR >= 1 && NBR <= NB, "column tiles");
   const int lane = threadIdx.x & 63, g = lane >> 4, r16 = lane & 15;
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
@@ -346,10 +352,9 @@ __device__ __forceinline__ void mfma_stage(const StageW<FMT, NMAT, RM>& W,
       }
 #pragma unroll
     for (int pl = 0; pl < PL; ++pl) {
-      if (pl >= npl) break;
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        if (nb >= nbr) break;
+      for (int nb = 0; nb < NBR; ++nb) {
+        if (DYN && nb >= nbr) break;
         const bf16x8_t Bv = lds_bf16x8(&xs[pl][nb * 16 + r16][64 * g + 8 * t]);
 #pragma unroll
         for (int m = 0; m < NMAT; ++m)
@@ -395,7 +400,9 @@ __global__ __launch_bounds__(64 * NW) void k_bmm(BArgs a) {
   __syncthreads();
   const int fl = s_flags;
   const int np = GU ? ((fl & 2) ? 3 : ((fl & 1) ? 2 : 1)) : 2;
-  const int ngr = (np + PL - 1) / PL;           // plane groups per K stage
+  static_assert(!GU || PL == 1 || NB == 1, "x planes staged one at a time in wide tiles");
+  static_assert(GU || PL == 2, "both h planes staged together");
+  const int ngr = (np + PL - 1) / PL;           // plane groups per K stage (every group holds PL planes)
 
   const int wave = tid >> 6, lane = tid & 63, g = lane >> 4, r16 = lane & 15;
   const int H = a.H, I = a.I, B = (FMT == MOE_FMT_MXFP4) ? 32 : 16;
@@ -442,27 +449,44 @@ __global__ __launch_bounds__(64 * NW) void k_bmm(BArgs a) {
   // per stage.  Plane groups beyond the first (wide tiles of non-bf16-exact
   // x only) stream the weights again.
   const int nkb = K / kSK;
-  for (int gr = 0; gr < ngr; ++gr) {
-    const int pl0 = gr * PL, npl = min(PL, np - pl0);
-    StageW<FMT, NMAT, RM> W0, W1;
-    StageB<NTOK, PL, NTHR> Bs;
-    load_stage<FMT, NMAT, RM>(codes, scales, coff, soff, 0, true, W0);
-    load_b<NTOK, PL, NTHR>(src, plane_bytes, K, s_row, cnt, pl0, np, 0, Bs);
-    load_stage<FMT, NMAT, RM>(codes, scales, coff, soff, 1, true, W1);
-    store_b<NTOK, PL, NTHR>(xs0, Bs);
-    load_b<NTOK, PL, NTHR>(src, plane_bytes, K, s_row, cnt, pl0, np, 1, Bs);
-    __syncthreads();
-    for (int kb = 0; kb < nkb; kb += 2) {
-      store_b<NTOK, PL, NTHR>(xs1, Bs);
-      load_b<NTOK, PL, NTHR>(src, plane_bytes, K, s_row, kb + 2 < nkb ? cnt : 0, pl0, np, kb + 2, Bs);
-      mfma_stage<FMT, NMAT, RM, NB, NTOK, PL>(W0, xs0, npl, nbr, acc);
-      load_stage<FMT, NMAT, RM>(codes, scales, coff, soff, kb + 2, kb + 2 < nkb, W0);
+  // the K loop for a compile-time count of column tiles
+  auto kloop = [&](auto nbr_c) {
+    constexpr int NBR = decltype(nbr_c)::value;
+    for (int gr = 0; gr < ngr; ++gr) {
+      const int pl0 = gr * PL;
+      StageW<FMT, NMAT, RM> W0, W1;
+      StageB<NTOK, PL, NTHR> Bs;
+      load_stage<FMT, NMAT, RM>(codes, scales, coff, soff, 0, true, W0);
+      load_b<NTOK, PL, NTHR>(src, plane_bytes, K, s_row, cnt, pl0, np, 0, Bs);
+      load_stage<FMT, NMAT, RM>(codes, scales, coff, soff, 1, true, W1);
+      store_b<NTOK, PL, NTHR>(xs0, Bs);
+      load_b<NTOK, PL, NTHR>(src, plane_bytes, K, s_row, cnt, pl0, np, 1, Bs);
       __syncthreads();
-      store_b<NTOK, PL, NTHR>(xs0, Bs);        // stage kb + 2 (zeros past the last)
-      load_b<NTOK, PL, NTHR>(src, plane_bytes, K, s_row, kb + 3 < nkb ? cnt : 0, pl0, np, kb + 3, Bs);
-      mfma_stage<FMT, NMAT, RM, NB, NTOK, PL>(W1, xs1, npl, nbr, acc);
-      load_stage<FMT, NMAT, RM>(codes, scales, coff, soff, kb + 3, kb + 3 < nkb, W1);
-      __syncthreads();
+      for (int kb = 0; kb < nkb; kb += 2) {
+        store_b<NTOK, PL, NTHR>(xs1, Bs);
+        load_b<NTOK, PL, NTHR>(src, plane_bytes, K, s_row, kb + 2 < nkb ? cnt : 0, pl0, np, kb + 2, Bs);
+        mfma_stage<FMT, NMAT, RM, NB, NTOK, PL, NBR, !GU>(W0, xs0, nbr, acc);
+        load_stage<FMT, NMAT, RM>(codes, scales, coff, soff, kb + 2, kb + 2 < nkb, W0);
+        __syncthreads();
+        store_b<NTOK, PL, NTHR>(xs0, Bs);        // stage kb + 2 (zeros past the last)
+        load_b<NTOK, PL, NTHR>(src, plane_bytes, K, s_row, kb + 3 < nkb ? cnt : 0, pl0, np, kb + 3, Bs);
+        mfma_stage<FMT, NMAT, RM, NB, NTOK, PL, NBR, !GU>(W1, xs1, nbr, acc);
+        load_stage<FMT, NMAT, RM>(codes, scales, coff, soff, kb + 3, kb + 3 < nkb, W1);
+        __syncthreads();
+      }
+    }
+  };
+  // gate/up: one instance per column-tile count; down (two planes, twice the
+  // fragments per step) keeps the runtime count, which spills no registers
+  static_assert(NB == 4, "column-tile dispatch below");
+  if (!GU) {
+    kloop(std::integral_constant<int, 4>{});
+  } else {
+    switch (nbr) {
+      case 1: kloop(std::integral_constant<int, 1>{}); break;
+      case 2: kloop(std::integral_constant<int, 2>{}); break;
+      case 3: kloop(std::integral_constant<int, 3>{}); break;
+      default: kloop(std::integral_constant<int, 4>{}); break;
     }
   }
 
