@@ -556,30 +556,49 @@ __global__ __launch_bounds__(256) void k_bcombine(BArgs a) {
 // ---------------------------------------------------------------------------
 // logits[t][e] = sum_h x[t][h] * W_r[e][h]: a 64-token x 64-expert tile per
 // workgroup, wave w owns tokens 16w..16w+15 against all 64 experts (four
-// 16x16 fp32 MFMA tiles), K in staged chunks of 32.
+// 16x16 fp32 MFMA tiles), K in staged chunks of 32.  Two LDS chunk buffers:
+// the next chunk is loaded into registers while the current one is
+// multiplied and stored into the other buffer before it, whose readers (the
+// previous chunk) finished at the last barrier, so one barrier per chunk.
 __global__ __launch_bounds__(256) void k_brouter(const float* x, const float* Wr, float* logits,
                                                  int C, int H, int E) {
-  __shared__ float xsm[64][kRK + 1];
-  __shared__ float wsm[64][kRK + 1];
+  __shared__ float xsm[2][64][kRK + 1];
+  __shared__ float wsm[2][64][kRK + 1];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, r16 = lane & 15;
   const int tb = blockIdx.y * 64, eb = blockIdx.x * 64;
+  float4 xv[2], wv[2];
+  auto fetch = [&](int k0) {                       // 512 float4 per matrix chunk
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int q = tid + 256 * u;
+      const int r = q >> 3, c4 = (q & 7) * 4;
+      const int t = tb + r, e = eb + r;
+      xv[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+      wv[u] = xv[u];
+      if (t < C) xv[u] = *reinterpret_cast<const float4*>(x + (size_t)t * H + k0 + c4);
+      if (e < E) wv[u] = *reinterpret_cast<const float4*>(Wr + (size_t)e * H + k0 + c4);
+    }
+  };
+  auto put = [&](int b) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int q = tid + 256 * u;
+      const int r = q >> 3, c4 = (q & 7) * 4;
+      xsm[b][r][c4] = xv[u].x; xsm[b][r][c4 + 1] = xv[u].y; xsm[b][r][c4 + 2] = xv[u].z; xsm[b][r][c4 + 3] = xv[u].w;
+      wsm[b][r][c4] = wv[u].x; wsm[b][r][c4 + 1] = wv[u].y; wsm[b][r][c4 + 2] = wv[u].z; wsm[b][r][c4 + 3] = wv[u].w;
+    }
+  };
   f32x4_t acc[4];
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) acc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  for (int k0 = 0; k0 < H; k0 += kRK) {
-    __syncthreads();
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int q = tid + 256 * u;                 // 512 float4 per matrix chunk
-      const int r = q >> 3, c4 = (q & 7) * 4;
-      const int t = tb + r, e = eb + r;
-      float4 xv = make_float4(0.f, 0.f, 0.f, 0.f), wv = xv;
-      if (t < C) xv = *reinterpret_cast<const float4*>(x + (size_t)t * H + k0 + c4);
-      if (e < E) wv = *reinterpret_cast<const float4*>(Wr + (size_t)e * H + k0 + c4);
-      xsm[r][c4] = xv.x; xsm[r][c4 + 1] = xv.y; xsm[r][c4 + 2] = xv.z; xsm[r][c4 + 3] = xv.w;
-      wsm[r][c4] = wv.x; wsm[r][c4 + 1] = wv.y; wsm[r][c4 + 2] = wv.z; wsm[r][c4 + 3] = wv.w;
-    }
-    __syncthreads();
+  fetch(0);
+  put(0);
+  if (kRK < H) fetch(kRK);
+  __syncthreads();
+  int b = 0;
+  for (int k0 = 0; k0 < H; k0 += kRK, b ^= 1) {
+    if (k0 + kRK < H) put(b ^ 1);
+    if (k0 + 2 * kRK < H) fetch(k0 + 2 * kRK);
     // The instruction adds its 4 products to the accumulator as 4 chained
     // FMAs (measured), so a chunk's products go into an accumulator of their
     // own (32 roundings) that is then added to the running sum: the longest
@@ -589,13 +608,14 @@ __global__ __launch_bounds__(256) void k_brouter(const float* x, const float* Wr
     for (int nb = 0; nb < 4; ++nb) part[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < kRK; kk += 4) {
-      const float av = xsm[16 * wave + r16][kk + g];
+      const float av = xsm[b][16 * wave + r16][kk + g];
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb)
-        part[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, wsm[nb * 16 + r16][kk + g], part[nb], 0, 0, 0);
+        part[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, wsm[b][nb * 16 + r16][kk + g], part[nb], 0, 0, 0);
     }
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) acc[nb] += part[nb];
+    __syncthreads();
   }
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) {
