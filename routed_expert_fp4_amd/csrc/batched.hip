@@ -456,11 +456,16 @@ __global__ __launch_bounds__(64 * NW) void k_bmm(BArgs a) {
       const int pl0 = gr * PL;
       StageW<FMT, NMAT, RM> W0, W1;
       StageB<NTOK, PL, NTHR> Bs;
+      // Issue order as at the loop's back edge (activations of the next
+      // stage, then the weights of the stage after it), so the compiler's
+      // count of outstanding loads agrees on both paths into the loop and
+      // its waits stay partial (a mismatch makes it wait for every load,
+      // the prefetches included).
       load_stage<FMT, NMAT, RM>(codes, scales, coff, soff, 0, true, W0);
       load_b<NTOK, PL, NTHR>(src, plane_bytes, K, s_row, cnt, pl0, np, 0, Bs);
-      load_stage<FMT, NMAT, RM>(codes, scales, coff, soff, 1, true, W1);
       store_b<NTOK, PL, NTHR>(xs0, Bs);
       load_b<NTOK, PL, NTHR>(src, plane_bytes, K, s_row, cnt, pl0, np, 1, Bs);
+      load_stage<FMT, NMAT, RM>(codes, scales, coff, soff, 1, true, W1);
       __syncthreads();
       for (int kb = 0; kb < nkb; kb += 2) {
         store_b<NTOK, PL, NTHR>(xs1, Bs);
