@@ -385,9 +385,9 @@ def bench_latent(args, wl):
     gbps = alg_bytes / (us_call * 1e-6) / 1e9
     fmt = "nvfp4" if wl.fmt == synth.FMT_NV else "mxfp4"
     if C == 1:
-        kernels = ("k_gemv (routed_down, with the shared selection), k_moe1 (router on the hidden "
-                   "state + routed experts, one launch), shared experts (k_sgu + k_sdn), "
-                   "k_gemv (norm + routed_up)")
+        kernels = ("k_lat_in (routed_down + the shared experts' gate/up, with the shared "
+                   "selection), k_moe1 (router on the hidden state + routed experts, one launch), "
+                   "k_lat_out (the shared experts' down + norm + routed_up)")
     else:
         kernels = ("k_gemv (routed_down, with the shared selection and dispatch table), "
                    "k_route + k_btopk (router and routed dispatch table), routed experts and "
