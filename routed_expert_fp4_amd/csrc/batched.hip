@@ -36,7 +36,8 @@
 //   k_bmm<GU>   per (tile, 256 rows of I): gate and up on MFMA, SwiGLU, h as
 //               two bf16 planes
 //   k_bmm<DN>   per (tile, 512 rows of H): down on MFMA, times the routing
-//               weight, one fp32 row per pair
+//               weight, one fp32 row per pair (k_bmm_dnp: the same as
+//               persistent workgroups where I spans four K stages or more)
 //   k_bcombine  out[t] = sum of its pairs' rows in slot order (deterministic)
 // and for the router of many tokens:
 //   k_brouter   logits = x * W_r^T with fp32 MFMA
@@ -60,6 +61,7 @@ constexpr int kNwDN = 16;            // down: waves per workgroup (512 rows)
 constexpr int kRmGUn = 2;            // narrow tiles: gate/up 128 rows per workgroup
 constexpr int kRmDNn = 4;            // narrow tiles: down 256 rows per workgroup
 constexpr int kRK = 32;              // router: K elements per staged chunk
+constexpr int kQueueDN = 16;         // meta[16]: the persistent down GEMM's item counter
 
 struct BArgs {
   const uint8_t* base;
@@ -211,6 +213,7 @@ __global__ __launch_bounds__(1024) void k_bscan(BArgs a) {
   if (e == 0) {
     a.boff[a.E] = (uint32_t)npairs;
     a.meta[0] = (uint32_t)ntiles;
+    a.meta[kQueueDN] = 0u;
   }
 }
 
@@ -537,6 +540,178 @@ __global__ __launch_bounds__(64 * NW) void k_bmm(BArgs a) {
             make_float4(wp * acc[0][r][nb][0], wp * acc[0][r][nb][1], wp * acc[0][r][nb][2],
                         wp * acc[0][r][nb][3]);
     }
+  }
+}
+
+// k_bmm_dnp: the down GEMM as persistent workgroups, one per CU, for K of
+// at least four stages.  A workgroup takes (tile, row block) items from a
+// counter in the workspace (item = tile * R + row block) and runs them as
+// one stream of K stages: the last stages of an item load the next item's
+// first weight and activation stages, so loads stay in flight across the
+// epilogue and the change of item, where a workgroup that ends and one that
+// starts leave the CU with none (per-workgroup clocks of k_bmm<DN> put ~13%
+// of its time there).  Item bookkeeping lives in three LDS slots (the item
+// being multiplied, the next one, whose loads start in this one's last
+// stages, and the one after it, taken from the counter and set up during
+// this one's first stages); the routing weights of an item's pairs are
+// staged with them.  Arithmetic, order of sums and outputs as k_bmm<DN>.
+template <int FMT, int RM, int NB, int NW>
+__global__ __launch_bounds__(64 * NW) void k_bmm_dnp(BArgs a) {
+  constexpr int NTOK = 16 * NB;
+  constexpr int NTHR = 64 * NW;
+  constexpr int PL = 2;                               // h: hi and lo planes
+  static_assert(NTOK * 32 % NTHR == 0, "activation stage split");
+  extern __shared__ __attribute__((aligned(16))) uint8_t bmm_lds[];   // two activation stages
+  uint16_t (*const xs0)[NTOK][kSStride] = reinterpret_cast<uint16_t (*)[NTOK][kSStride]>(bmm_lds);
+  uint16_t (*const xs1)[NTOK][kSStride] = xs0 + PL;
+  __shared__ int s_pair[3][NTOK], s_row[3][NTOK];
+  __shared__ float s_wgt[3][NTOK];
+  __shared__ int s_item[3], s_e[3], s_cnt[3];
+
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r16 = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: the views below are scalar
+  const int H = a.H, I = a.I, B = (FMT == MOE_FMT_MXFP4) ? 32 : 16;
+  const int K = I, N = H;
+  const int R = N / (16 * RM * NW);
+  const int nitems = (int)a.meta[0] * R;
+  const int nkb = K / kSK;                            // even, >= 4
+  uint32_t* const q = a.meta + kQueueDN;
+  const size_t CK = (size_t)a.C * a.k;
+  const uint32_t plane_bytes = (uint32_t)(CK * I * 2);
+  const __amdgpu_buffer_rsrc_t src = view(reinterpret_cast<const uint8_t*>(a.hp), plane_bytes * 2u);
+  const uint32_t cbytes = (uint32_t)N * (K / 2), sbytes = (uint32_t)N * (K / B);
+
+  // slot sl <- item it (it >= 0): expert, pair count, pairs, their rows and
+  // routing weights (times the NVFP4 global)
+  auto setup = [&](int sl, int it) {
+    const int tile = it / R;
+    const int e = a.tiles[2 * tile], t0 = a.tiles[2 * tile + 1];
+    const int cnt = min(NTOK, (int)a.count[e] - t0);
+    if (tid < NTOK) {
+      const int pr = tid < cnt ? a.perm[a.boff[e] + t0 + tid] : -1;
+      s_pair[sl][tid] = pr;
+      s_row[sl][tid] = pr;
+      float gd = 1.0f;
+      if (FMT == MOE_FMT_NVFP4 && pr >= 0)
+        gd = reinterpret_cast<const float*>(a.base + (size_t)e * a.stride + a.off[MOE_T_GLOBALS])[2];
+      s_wgt[sl][tid] = pr >= 0 ? a.w[pr] * gd : 0.0f;
+    }
+    if (tid == 0) {
+      s_e[sl] = e;
+      s_cnt[sl] = cnt;
+    }
+  };
+  // this lane's offsets from its wave's first row (the same for every item)
+  uint32_t coff[RM], soff[RM];
+#pragma unroll
+  for (int r = 0; r < RM; ++r) {
+    coff[r] = (uint32_t)(16 * r + r16) * (K / 2) + g * 32;
+    soff[r] = (uint32_t)(16 * r + r16) * (K / B) + g * (64 / B);
+  }
+  // the weight views of item it from this wave's first row on (uniform
+  // values only; it < 0: empty views, no loads)
+  struct View {
+    __amdgpu_buffer_rsrc_t codes[1], scales[1];
+    int cnt, sl;
+  };
+  auto view_of = [&](int sl, int it, View& v) {
+    v.sl = sl;
+    v.cnt = __builtin_amdgcn_readfirstlane(it >= 0 ? s_cnt[sl] : 0);
+    const int e = __builtin_amdgcn_readfirstlane(it >= 0 ? s_e[sl] : 0);
+    const int row0 = (it >= 0 ? it % R : 0) * (16 * RM * NW) + wave * (16 * RM);
+    const uint8_t* rec = a.base + (size_t)e * a.stride;
+    v.codes[0] = view(rec + a.off[MOE_T_DOWN_CODES] + (size_t)row0 * (K / 2),
+                      it >= 0 ? cbytes - (uint32_t)row0 * (K / 2) : 0u);
+    v.scales[0] = view(rec + a.off[MOE_T_DOWN_SCALES] + (size_t)row0 * (K / B),
+                       it >= 0 ? sbytes - (uint32_t)row0 * (K / B) : 0u);
+  };
+
+  // items 0 and 1 of this workgroup
+  if (tid == 0) {
+    const uint32_t i0 = atomicAdd(q, 1u), i1 = atomicAdd(q, 1u);
+    s_item[0] = i0 < (uint32_t)nitems ? (int)i0 : -1;
+    s_item[1] = i1 < (uint32_t)nitems ? (int)i1 : -1;
+  }
+  __syncthreads();
+  int cur = __builtin_amdgcn_readfirstlane(s_item[0]), nxt = __builtin_amdgcn_readfirstlane(s_item[1]);
+  if (cur < 0) return;
+  setup(0, cur);
+  if (nxt >= 0) setup(1, nxt);
+  __syncthreads();
+  View vc, vn;
+  view_of(0, cur, vc);
+  view_of(1, nxt, vn);
+
+  StageW<FMT, 1, RM> W0, W1;
+  StageB<NTOK, PL, NTHR> Bs;
+  load_stage<FMT, 1, RM>(vc.codes, vc.scales, coff, soff, 0, true, W0);
+  load_b<NTOK, PL, NTHR>(src, plane_bytes, K, s_row[vc.sl], vc.cnt, 0, PL, 0, Bs);
+  store_b<NTOK, PL, NTHR>(xs0, Bs);
+  load_b<NTOK, PL, NTHR>(src, plane_bytes, K, s_row[vc.sl], vc.cnt, 0, PL, 1, Bs);
+  load_stage<FMT, 1, RM>(vc.codes, vc.scales, coff, soff, 1, true, W1);
+  __syncthreads();
+
+  int seq = 0;                                        // this workgroup's item count
+  for (;;) {
+    f32x4_t acc[1][RM][NB];
+#pragma unroll
+    for (int r = 0; r < RM; ++r)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) acc[0][r][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const int nbr = (vc.cnt + 15) >> 4;
+    const int sl2 = (seq + 2) % 3;                    // slot of the item after the next
+    for (int kb = 0; kb < nkb; kb += 2) {
+      const bool last = kb + 2 >= nkb;
+      store_b<NTOK, PL, NTHR>(xs1, Bs);
+      if (!last) load_b<NTOK, PL, NTHR>(src, plane_bytes, K, s_row[vc.sl], vc.cnt, 0, PL, kb + 2, Bs);
+      else load_b<NTOK, PL, NTHR>(src, plane_bytes, K, s_row[vn.sl], vn.cnt, 0, PL, 0, Bs);
+      mfma_stage<FMT, 1, RM, NB, NTOK, PL, NB, true>(W0, xs0, nbr, acc);
+      if (!last) load_stage<FMT, 1, RM>(vc.codes, vc.scales, coff, soff, kb + 2, true, W0);
+      else load_stage<FMT, 1, RM>(vn.codes, vn.scales, coff, soff, 0, nxt >= 0, W0);
+      __syncthreads();
+      // after the first barrier of an item the slot of the item before it is
+      // free: take the item after the next from the counter
+      if (kb == 0 && tid == 0) {
+        const uint32_t i2 = nxt >= 0 ? atomicAdd(q, 1u) : 0xFFFFFFFFu;
+        s_item[sl2] = i2 < (uint32_t)nitems ? (int)i2 : -1;
+      }
+      // ... and set it up in the second stage pair (visible from the next
+      // barrier on, before the next item's last stages load from it)
+      if (kb == 2) {
+        const int it2 = __builtin_amdgcn_readfirstlane(s_item[sl2]);
+        if (it2 >= 0) setup(sl2, it2);
+      }
+      store_b<NTOK, PL, NTHR>(xs0, Bs);
+      if (!last) load_b<NTOK, PL, NTHR>(src, plane_bytes, K, s_row[vc.sl], vc.cnt, 0, PL, kb + 3, Bs);
+      else load_b<NTOK, PL, NTHR>(src, plane_bytes, K, s_row[vn.sl], vn.cnt, 0, PL, 1, Bs);
+      mfma_stage<FMT, 1, RM, NB, NTOK, PL, NB, true>(W1, xs1, nbr, acc);
+      // (the next item's second weight stage is loaded after the epilogue,
+      // which then holds fewer registers)
+      if (!last) load_stage<FMT, 1, RM>(vc.codes, vc.scales, coff, soff, kb + 3, true, W1);
+      __syncthreads();
+    }
+    // epilogue of the current item: weighted rows out, one per pair
+    {
+      const int orow0 = (cur % R) * (16 * RM * NW) + wave * (16 * RM) + 4 * g;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int pr = s_pair[vc.sl][nb * 16 + r16];
+        if (pr < 0) continue;
+        const float wp = s_wgt[vc.sl][nb * 16 + r16];
+#pragma unroll
+        for (int r = 0; r < RM; ++r)
+          *reinterpret_cast<float4*>(a.part + (size_t)pr * H + orow0 + 16 * r) =
+              make_float4(wp * acc[0][r][nb][0], wp * acc[0][r][nb][1], wp * acc[0][r][nb][2],
+                          wp * acc[0][r][nb][3]);
+      }
+    }
+    if (nxt < 0) break;
+    load_stage<FMT, 1, RM>(vn.codes, vn.scales, coff, soff, 1, true, W1);
+    ++seq;
+    cur = nxt;
+    vc = vn;
+    nxt = __builtin_amdgcn_readfirstlane(s_item[sl2]);
+    view_of(sl2, nxt, vn);
   }
 }
 
@@ -1011,6 +1186,22 @@ moe_status launch_bmm(const BArgs& a, dim3 grid, hipStream_t st) {
     attr_set[dev].store(true, std::memory_order_relaxed);
   }
   hipLaunchKernelGGL((k_bmm<FMT, GU, RM, NB, NW>), grid, dim3(64 * NW), bytes, st, a);
+  return MOE_OK;
+}
+
+template <int FMT, int RM, int NB, int NW>
+moe_status launch_bmm_dnp(const BArgs& a, dim3 grid, hipStream_t st) {
+  constexpr int bytes = 2 * 2 * 16 * NB * kSStride * 2;
+  static std::atomic<bool> attr_set[64];   // per device, set once (concurrent setters agree)
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (!attr_set[dev].load(std::memory_order_relaxed)) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(k_bmm_dnp<FMT, RM, NB, NW>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, bytes) != hipSuccess)
+      return MOE_ERR_DEVICE;
+    attr_set[dev].store(true, std::memory_order_relaxed);
+  }
+  hipLaunchKernelGGL((k_bmm_dnp<FMT, RM, NB, NW>), grid, dim3(64 * NW), bytes, st, a);
   return MOE_OK;
 }
 
@@ -1567,6 +1758,7 @@ moe_status launch_batched_experts(const moe_bank* b, const float* x, int C, int 
   hipLaunchKernelGGL(k_bscan, dim3(1), dim3(1024), 0, st, a);
   hipLaunchKernelGGL(k_bscatter, dim3((CK + 255) / 256), dim3(256), 0, st, a);
   const dim3 ggu(I / (16 * kRmGU * kNwGU), maxt), gdn(H / (16 * kRmDN * kNwDN), maxt);
+  const dim3 gpers(dstream_grid());                // persistent down GEMM: one workgroup per CU
   const dim3 ggun(I / (64 * kRmGUn), maxt), gdnn(H / (64 * kRmDNn), maxt);
 #define RF4_BMM(F)                                                                        \
   do {                                                                                    \
@@ -1576,7 +1768,9 @@ moe_status launch_batched_experts(const moe_bank* b, const float* x, int C, int 
       if (m != MOE_OK) return m;                                                          \
     } else {                                                                              \
       moe_status m = launch_bmm<F, true, kRmGU, 4, kNwGU>(a, ggu, st);                    \
-      if (m == MOE_OK) m = launch_bmm<F, false, kRmDN, 4, kNwDN>(a, gdn, st);             \
+      if (m == MOE_OK)                                                                    \
+        m = I >= 4 * kSK ? launch_bmm_dnp<F, kRmDN, 4, kNwDN>(a, gpers, st)               \
+                         : launch_bmm<F, false, kRmDN, 4, kNwDN>(a, gdn, st);             \
       if (m != MOE_OK) return m;                                                          \
     }                                                                                     \
   } while (0)

@@ -65,7 +65,7 @@ inline WsLayout ws_layout(int E, int H, int I, int k, int C) {
   L.bcount = o;  o = align256(o + (size_t)E * sizeof(uint32_t));
   L.bcursor = o; o = align256(o + (size_t)E * sizeof(uint32_t));
   L.boff = o;    o = align256(o + (size_t)(E + 1) * sizeof(uint32_t));
-  L.bmeta = o;   o = align256(o + 16 * sizeof(uint32_t));
+  L.bmeta = o;   o = align256(o + 32 * sizeof(uint32_t));   // tile count, item counter
   L.btile = o;   o = align256(o + batch_max_tiles(E, k, C) * 2 * sizeof(int32_t));
   L.perm = o;    o = align256(o + CK * sizeof(int32_t));
   L.xp = o;      o = align256(o + 3 * (size_t)C * H * sizeof(uint16_t));
