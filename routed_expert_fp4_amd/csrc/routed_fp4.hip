@@ -762,7 +762,9 @@ constexpr int kRouterRU = kMaxH1 / 2 / 4 / 64;     // float4 loads per lane (max
 
 __device__ __forceinline__ int router_half_row(const Moe1Args& a) {
   const int hpw = (2 * a.n_router + kG1 - 1) / kG1;
-  const int wave = threadIdx.x >> 6;
+  // uniform per wave (readfirstlane), so the half row's view is scalar and
+  // its loads need no per-lane loop
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hr = blockIdx.x * hpw + wave;
   return (wave < hpw && hr < 2 * a.n_router) ? hr : -1;
 }
