@@ -1423,13 +1423,17 @@ __device__ __forceinline__ void dmma_rows(const __amdgpu_buffer_rsrc_t (&crs)[NR
       }
     }
   };
+  // Whole groups of kDPipe stages, with no exit between them: stages past
+  // the last load zeros without memory traffic and multiply nothing (the
+  // crow < rows test), and a straight loop body lets the compiler keep its
+  // waits partial (an exit inside the group made it wait for nearly every
+  // load in flight at the end of each pass through the loop).
   const int nst = (rows * kch + kDSC - 1) / kDSC;
 #pragma unroll
   for (int j = 0; j < kDPipe - 1; ++j) load(q[j], sc[j]);
   for (int st0 = 0; st0 < nst; st0 += kDPipe) {
 #pragma unroll
     for (int j = 0; j < kDPipe; ++j) {
-      if (st0 + j >= nst) break;
       __builtin_amdgcn_sched_barrier(0);
       load(q[(j + kDPipe - 1) % kDPipe], sc[(j + kDPipe - 1) % kDPipe]);
       __builtin_amdgcn_sched_barrier(0);
