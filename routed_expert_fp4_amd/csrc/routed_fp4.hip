@@ -285,36 +285,61 @@ __global__ __launch_bounds__(kWG) void k_route(RouteArgs a) {
   __shared__ float xs[kRouteXs];
   __shared__ TopkShared S;
   __shared__ int s_last;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: the row view below is scalar
 
   if (a.x) {
     // x tiles of KT columns per token (KT: a multiple of 256 that fits the
-    // call's C tokens in LDS, at most kRouteWt); each wave's row loads of a
-    // tile are issued before the tile is staged, so the two latencies overlap
+    // call's C tokens in LDS, at most kRouteWt).  A tile's x loads (all of
+    // them at once: at most kRouteXs / 4 float4, kRouteXs / (4 kWG) per
+    // thread) are issued first and the wave's row loads after them, so
+    // storing x into LDS waits for x alone (loads complete in issue order)
+    // while the rows stay in flight.
     const int KT = min(kRouteWt, (kRouteXs / a.C) & ~255);
     const int b = blockIdx.x;
     const int rbk = b / a.ksplit, ks = b - rbk * a.ksplit;
     const int e = rbk * 4 + wave;
     const int k0 = ks * a.kper;
     const int k1 = min(a.H, k0 + a.kper);
-    const float4* wrow = reinterpret_cast<const float4*>(a.Wr + (size_t)(e < a.E ? e : 0) * a.H);
+    // x of all tokens, and this wave's router row (empty past the last expert)
+    const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(a.x), (short)0, a.C * a.H * 4, 0x00020000);
+    const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(a.Wr + (size_t)(e < a.E ? e : 0) * a.H), (short)0, e < a.E ? a.H * 4 : 0,
+        0x00020000);
     float acc[CM];
 #pragma unroll
     for (int t = 0; t < CM; ++t) acc[t] = 0.0f;
     for (int kt = k0; kt < k1; kt += KT) {
       const int kn = min(KT, k1 - kt);
       const int n4 = kn >> 2;
+      constexpr int kXv = kRouteXs / 4 / kWG;  // float4 of the x tile per thread
+      const int n4t = (a.C * kn) >> 2;
+      // buffer loads, every one issued (those out of range read zeros
+      // without memory traffic), so the compiler counts them exactly
+      float4 xv[kXv];
+#pragma unroll
+      for (int u = 0; u < kXv; ++u) {
+        const int i = 4 * (tid + kWG * u), t = i / kn, col = i - t * kn;
+        const uint32_t o = tid + kWG * u < n4t ? (uint32_t)((t * a.H + kt + col) * 4) : 0x80000000u;
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(xrs, (int)o, 0, 0);
+        xv[u] = make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]),
+                            __uint_as_float(v[3]));
+      }
       float4 wv[kRouteWt / 256];
 #pragma unroll
       for (int u = 0; u < kRouteWt / 256; ++u) {
         const int c = lane + 64 * u;
-        wv[u] = (e < a.E && c < n4) ? wrow[(kt >> 2) + c] : make_float4(0.f, 0.f, 0.f, 0.f);
+        const uint32_t o = c < n4 ? (uint32_t)((kt + 4 * c) * 4) : 0x80000000u;
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(wrs, (int)o, 0, 0);
+        wv[u] = make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]),
+                            __uint_as_float(v[3]));
       }
       __syncthreads();                         // the previous tile's products are done
-      for (int i = tid * 4; i < a.C * kn; i += kWG * 4) {
-        const int t = i / kn, col = i - t * kn;
-        *reinterpret_cast<float4*>(&xs[t * KT + col]) =
-            *reinterpret_cast<const float4*>(&a.x[(size_t)t * a.H + kt + col]);
+#pragma unroll
+      for (int u = 0; u < kXv; ++u) {
+        const int i = 4 * (tid + kWG * u), t = i / kn, col = i - t * kn;
+        if (tid + kWG * u < n4t) *reinterpret_cast<float4*>(&xs[t * KT + col]) = xv[u];
       }
       __syncthreads();
       if (e < a.E) {
