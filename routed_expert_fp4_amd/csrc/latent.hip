@@ -53,10 +53,18 @@ constexpr int kGemvWG = 256;
 // Weight bytes are read once per call: non-temporal loads keep them from
 // displacing the activations in the caches (1 to 1.5 us per launch on the
 // K3 latent shape against plain loads).
-typedef unsigned int nt_u32x4_t __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ uint4 load_nt16(const uint8_t* p) {
-  const nt_u32x4_t t = __builtin_nontemporal_load(reinterpret_cast<const nt_u32x4_t*>(p));
-  return make_uint4(t.x, t.y, t.z, t.w);
+// Weight loads as buffer loads that are always issued: an offset past the
+// view (kOutside) reads zeros without memory traffic, so no load sits in a
+// branch and the compiler's count of loads in flight stays exact (with
+// loads in branches it waits for all of them where they join, before the
+// next stream's loads are even issued).
+constexpr uint32_t kOutside = 0x80000000u;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t lview(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t v, uint32_t off) {
+  const auto t = __builtin_amdgcn_raw_buffer_load_b128(v, (int)off, 0, kCachePolicyNt);
+  return make_uint4(t[0], t[1], t[2], t[3]);
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -108,7 +116,7 @@ __device__ void write_shared_selection(const GemvArgs& a) {
 // arithmetic, and x (with gamma applied) comes straight from L2 into
 // registers for each chunk, in groups of up to 4 tokens.  With the norm, the
 // same x values give each token's sum of squares over K (ss).
-template <int RB, int CM, int NCH>
+template <int RB, int CM, int NCH, bool ONE = false>
 __device__ __forceinline__ void gemv_dot(const GemvArgs& a, int n0, float (&acc)[RB][CM],
                                          float (&ss)[CM]) {
   constexpr int TG = CM < 4 ? CM : 4;                 // tokens per x group
@@ -122,18 +130,21 @@ __device__ __forceinline__ void gemv_dot(const GemvArgs& a, int n0, float (&acc)
     for (int r = 0; r < RB; ++r) acc[r][t] = 0.0f;
   }
 
-  for (int c0 = 0; c0 < K8; c0 += kGemvWG * NCH) {
+  __amdgpu_buffer_rsrc_t wv[RB];                     // row n0 + r (empty past N)
+#pragma unroll
+  for (int r = 0; r < RB; ++r)
+    wv[r] = lview(a.W + (size_t)(n0 + r < N ? n0 + r : 0) * K, n0 + r < N ? (uint32_t)K * 2u : 0u);
+  // ONE: K fits one slab (K / 8 <= kGemvWG * NCH); then there is no loop,
+  // and a caller's weight loads issued before this call stay in flight with
+  // these (a loop's entry makes the compiler wait for them)
+  const int c0end = ONE ? 1 : K8;
+  for (int c0 = 0; c0 < c0end; c0 += kGemvWG * NCH) {
     uint4 wq[RB][NCH];
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
       const int c = c0 + tid + kGemvWG * j;
 #pragma unroll
-      for (int r = 0; r < RB; ++r) {
-        const int n = n0 + r;
-        wq[r][j] = (c < K8 && n < N)
-                       ? load_nt16(reinterpret_cast<const uint8_t*>(a.W + (size_t)n * K) + 16 * c)
-                       : make_uint4(0u, 0u, 0u, 0u);
-      }
+      for (int r = 0; r < RB; ++r) wq[r][j] = bload16(wv[r], c < K8 ? 16u * (uint32_t)c : kOutside);
     }
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
@@ -185,7 +196,7 @@ __device__ __forceinline__ void gemv_dot(const GemvArgs& a, int n0, float (&acc)
 // Block blk of the mat-vec: rows blk*RB .. blk*RB+RB-1.  The per-thread
 // partial sums are reduced over the wave (DPP) and then over the four waves
 // in order.
-template <int RB, int CM, int NCH>
+template <int RB, int CM, int NCH, bool ONE = false>
 __device__ __forceinline__ void gemv_block(const GemvArgs& a, int blk) {
   __shared__ float s_part[kGemvWG / 64][RB * CM + CM];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -195,7 +206,7 @@ __device__ __forceinline__ void gemv_block(const GemvArgs& a, int blk) {
   if (a.sel_idx && blk == 0) write_shared_selection(a);
 
   float acc[RB][CM], ss[CM];
-  gemv_dot<RB, CM, NCH>(a, n0, acc, ss);
+  gemv_dot<RB, CM, NCH, ONE>(a, n0, acc, ss);
 
 #pragma unroll
   for (int t = 0; t < CM; ++t) {
@@ -290,10 +301,12 @@ __device__ __forceinline__ float sdot32(const uint4& q, uint32_t sc, const float
   return b[0] * __builtin_amdgcn_cvt_f32_fp8((int)sc, 0) + b[1] * __builtin_amdgcn_cvt_f32_fp8((int)sc, 1);
 }
 
+// the scale(s) of 32-element chunk c at byte offset o of view v (o past the
+// view: zeros): one e8m0 byte (MXFP4) or two e4m3 bytes (NVFP4)
 template <int FMT>
-__device__ __forceinline__ uint32_t sscale(const uint8_t* srow, int c) {
-  if (FMT == MOE_FMT_MXFP4) return __builtin_nontemporal_load(srow + c);
-  return __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(srow + 2 * c));
+__device__ __forceinline__ uint32_t sscale(__amdgpu_buffer_rsrc_t v, uint32_t o) {
+  if (FMT == MOE_FMT_MXFP4) return __builtin_amdgcn_raw_buffer_load_b8(v, (int)o, 0, kCachePolicyNt);
+  return __builtin_amdgcn_raw_buffer_load_b16(v, (int)o, 0, kCachePolicyNt);
 }
 
 // gate and up rows i0 .. i0+3 of shared expert blockIdx.y: the 256 threads
@@ -307,8 +320,14 @@ __device__ __forceinline__ void sgu_block(const SArgs& a, int j, int i0) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int H = a.H, nch = H / 32;
   const uint8_t* rec = a.base + (size_t)j * a.stride;
-  const uint8_t* cb[2] = {rec + a.off[MOE_T_GATE_CODES], rec + a.off[MOE_T_UP_CODES]};
-  const uint8_t* sbp[2] = {rec + a.off[MOE_T_GATE_SCALES], rec + a.off[MOE_T_UP_SCALES]};
+  // rows i0 .. i0 + kSRowsGU - 1 of the gate and up codes and scales
+  const uint32_t cbytes = (uint32_t)kSRowsGU * (H / 2), sbytes = (uint32_t)kSRowsGU * (H / B);
+  const __amdgpu_buffer_rsrc_t cv[2] = {
+      lview(rec + a.off[MOE_T_GATE_CODES] + (size_t)i0 * (H / 2), cbytes),
+      lview(rec + a.off[MOE_T_UP_CODES] + (size_t)i0 * (H / 2), cbytes)};
+  const __amdgpu_buffer_rsrc_t sv[2] = {
+      lview(rec + a.off[MOE_T_GATE_SCALES] + (size_t)i0 * (H / B), sbytes),
+      lview(rec + a.off[MOE_T_UP_SCALES] + (size_t)i0 * (H / B), sbytes)};
   uint4 q[MAXCH][kSRowsGU][2];
   uint32_t sc[MAXCH][kSRowsGU][2];
 #pragma unroll
@@ -318,14 +337,8 @@ __device__ __forceinline__ void sgu_block(const SArgs& a, int j, int i0) {
     for (int r = 0; r < kSRowsGU; ++r)
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
-        if (c < nch) {
-          const size_t row = (size_t)(i0 + r);
-          q[u][r][m] = load_nt16(cb[m] + row * (H / 2) + 16 * c);
-          sc[u][r][m] = sscale<FMT>(sbp[m] + row * (H / B), c);
-        } else {
-          q[u][r][m] = make_uint4(0u, 0u, 0u, 0u);
-          sc[u][r][m] = 0u;
-        }
+        q[u][r][m] = bload16(cv[m], c < nch ? (uint32_t)(r * (H / 2) + 16 * c) : kOutside);
+        sc[u][r][m] = sscale<FMT>(sv[m], c < nch ? (uint32_t)(r * (H / B) + (32 / B) * c) : kOutside);
       }
   }
   float acc[kSRowsGU][2];
@@ -382,21 +395,21 @@ template <int FMT, int RD, int MAXCH>
 __device__ __forceinline__ void sdn_load(const SArgs& a, int n0, SdnW<RD, MAXCH>& w) {
   constexpr int B = FMT == MOE_FMT_MXFP4 ? 32 : 16;
   const int tid = threadIdx.x, I = a.I, nchI = I / 32, ntot = a.ns * nchI;
+  // the whole shared bank (ns * stride < 2^31 bytes, checked on the host)
+  const __amdgpu_buffer_rsrc_t bv = lview(a.base, (uint32_t)(a.ns * a.stride));
 #pragma unroll
   for (int u = 0; u < MAXCH; ++u) {
     const int cc = tid + 256 * u;
     const int j = cc < ntot ? cc / nchI : 0, c = cc < ntot ? cc - j * nchI : 0;
-    const uint8_t* rec = a.base + (size_t)j * a.stride;
+    const uint32_t rec = (uint32_t)(j * a.stride);
 #pragma unroll
     for (int r = 0; r < RD; ++r) {
-      if (cc < ntot) {
-        const size_t row = (size_t)(n0 + r);
-        w.q[u][r] = load_nt16(rec + a.off[MOE_T_DOWN_CODES] + row * (I / 2) + 16 * c);
-        w.sc[u][r] = sscale<FMT>(rec + a.off[MOE_T_DOWN_SCALES] + row * (I / B), c);
-      } else {
-        w.q[u][r] = make_uint4(0u, 0u, 0u, 0u);
-        w.sc[u][r] = 0u;
-      }
+      const uint32_t row = (uint32_t)(n0 + r);
+      w.q[u][r] = bload16(bv, cc < ntot ? rec + (uint32_t)a.off[MOE_T_DOWN_CODES] + row * (I / 2) + 16u * c
+                                        : kOutside);
+      w.sc[u][r] = sscale<FMT>(bv, cc < ntot ? rec + (uint32_t)a.off[MOE_T_DOWN_SCALES] + row * (I / B) +
+                                                   (uint32_t)((32 / B) * c)
+                                             : kOutside);
     }
   }
 }
@@ -439,7 +452,7 @@ template <int FMT, int MAXCH>
 __global__ __launch_bounds__(256) void k_lat_in(GemvArgs g, SArgs s, int nA) {
   const int b = blockIdx.x;
   if (b < nA) {
-    gemv_block<kLatRowsA, 1, 4>(g, b);
+    gemv_block<kLatRowsA, 1, 4, true>(g, b);
   } else {
     const int per = s.I / kSRowsGU, q = b - nA;
     sgu_block<FMT, MAXCH>(s, q / per, (q - (q / per) * per) * kSRowsGU);
@@ -460,7 +473,7 @@ __global__ __launch_bounds__(256) void k_lat_out(GemvArgs g, SArgs s) {
   SdnW<RB, MAXCH> w;
   sdn_load<FMT, RB, MAXCH>(s, n0, w);
   float acc[RB][1], ss[1];
-  gemv_dot<RB, 1, 2>(g, n0, acc, ss);
+  gemv_dot<RB, 1, 2, true>(g, n0, acc, ss);
   float sacc[RB];
   sdn_dot<FMT, RB, MAXCH>(s, w, sacc);
 #pragma unroll
@@ -487,6 +500,7 @@ __global__ __launch_bounds__(256) void k_lat_out(GemvArgs g, SArgs s) {
 
 bool shared1_ok(const moe_bank* S, int H) {
   return S->hidden == H && H % 32 == 0 && S->inter % 32 == 0 && H / 32 <= 256 * kSMaxCh &&
+         (int64_t)S->num_experts * S->expert_stride < ((int64_t)1 << 31) &&
          S->num_experts * (S->inter / 32) <= 256 * kSMaxCh && H % kSRowsDN == 0 &&
          S->inter % kSRowsGU == 0 && (S->format == MOE_FMT_MXFP4 || S->format == MOE_FMT_NVFP4);
 }
@@ -618,7 +632,10 @@ moe_status moe_latent_layer_fwd(const moe_latent_layer* layer, const float* x, i
   g.sel_idx = sidx; g.sel_w = sw; g.ns = ns;     // the shared experts' selection
   // and, where the decode-batch streams take the shared bank, its dispatch
   // table (every token, every shared expert), so no dispatch launch is needed
-  const bool shared_one = C == 1 && bank_status(&S) == MOE_OK && shared1_ok(&S, H);
+  // (the one-token launches take W_down and W_up in one slab each: H <= 8192
+  // and L <= 4096)
+  const bool shared_one = C == 1 && bank_status(&S) == MOE_OK && shared1_ok(&S, H) &&
+                          H / 8 <= kGemvWG * 4 && L / 8 <= kGemvWG * 2;
   const bool shared_streams =
       !shared_one && bank_status(&S) == MOE_OK && batched_decode_shape(&S, C);
   const WsLayout Ls = ws_layout(ns, S.hidden, S.inter, ns, C);
