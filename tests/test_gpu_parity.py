@@ -381,6 +381,28 @@ def test_batched_layer_parity(C, fmt, routing):
     bf16-exact activations (one activation plane), natural ones fp32 (three)."""
     wl = _small_prefill(C, fmt, routing)
     say(f"[batched] C={C} fmt={fmt} {routing}")
+    _batched_layer_check(wl, routing)
+
+
+@pytest.mark.parametrize("I,C,fmt,routing", [(1024, 200, synth.FMT_NV, "zipf"),
+                                             (1536, 130, synth.FMT_MX, "natural"),
+                                             (1536, 257, synth.FMT_NV, "zipf")])
+def test_batched_persistent_down_parity(I, C, fmt, routing):
+    """An inner width of four 256-wide K stages or more, where the down GEMM
+    runs as persistent workgroups taking (tile, row block) items from a
+    counter and loading each next item's first stages during the current
+    one's last: 64 experts, top-8, H 1024 (two 512-row blocks), element by
+    element.  Zipf cases put 181 and 235 tokens on the hottest expert (3 and
+    4 tiles of 64, the last partial); natural routing gives many one-tile
+    experts, so consecutive items change expert at almost every step."""
+    wl = synth.Workload(f"bdnp_{I}_{C}", fmt, 64, 8, 1024, I, C, 1, routing,
+                        1.0 if routing == "zipf" else 0.0, routing == "zipf")
+    say(f"[batched, persistent down] I={I} C={C} fmt={fmt} {routing}")
+    _batched_layer_check(wl, routing)
+
+
+def _batched_layer_check(wl, routing):
+    C = wl.C
     spec = wl.bank(0)
     bank = cached_bank(spec)
     Wr, x = synth.layer_inputs(wl, 0)
